@@ -1,0 +1,109 @@
+// Internal declarations shared by the host library and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+struct kvf8_cache {
+    int32_t layers = 0;
+    int64_t num_blocks = 0;
+    int32_t block_size = 0;
+    int32_t kv_heads = 0;
+    int32_t head_dim = 0;
+    size_t pool_bytes = 0;          // bytes of one layer's K pool (same for V)
+    uint8_t *k_base = nullptr;      // [layers][pool_bytes]
+    uint8_t *v_base = nullptr;
+    bool owned = false;
+    int device = 0;
+    std::vector<float> k_scale, v_scale, k_inv, v_inv;
+    std::vector<int32_t> free_list;  // LIFO: back() is handed out next
+    std::vector<uint8_t> allocated;
+};
+
+namespace kvf8 {
+
+// ---------------------------------------------------------------- store
+struct StoreArgs {
+    const uint16_t *k;
+    const uint16_t *v;
+    int64_t k_stride;        // elements between token rows
+    int64_t v_stride;
+    const int64_t *slots;
+    int64_t num_tokens;
+    uint8_t *k_pool;         // this layer
+    uint8_t *v_pool;
+    float k_inv;
+    float v_inv;
+    int32_t kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+};
+hipError_t launch_store(const StoreArgs &a, hipStream_t stream);
+
+// ---------------------------------------------------------------- decode
+struct DecodeArgs {
+    const uint16_t *q;
+    const uint8_t *k_pool;
+    const uint8_t *v_pool;
+    const int32_t *block_tables;
+    const int32_t *seq_lens;
+    void *out;
+    float *partials;         // [num_seqs][q_heads][splits][head_dim + 2] or null
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t q_heads;
+    int32_t kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t splits;          // chunks per (seq, kv-head)
+    int32_t chunk_tokens;    // tokens per chunk (multiple of the block size)
+    float qk_scale;          // k_scale * sm_scale * log2(e)
+    float v_scale;
+    int32_t out_bf16;
+};
+// Number of splits and chunk length the decode uses for this shape.
+void decode_plan(int32_t num_seqs, int32_t kv_heads, int32_t head_dim, int32_t block_size,
+                 int32_t max_seq_len, int32_t *splits, int32_t *chunk_tokens);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+// ---------------------------------------------------------------- K-shift
+struct KShiftArgs {
+    uint8_t *k_pool;
+    const int64_t *slots;
+    int64_t n_slots;
+    int32_t kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t rot_dim;
+    int32_t neox;
+    float cos_t[128];
+    float sin_t[128];
+};
+hipError_t launch_kshift(const KShiftArgs &a, hipStream_t stream);
+
+// ---------------------------------------------------------------- prefill
+struct PrefillArgs {
+    const uint16_t *q;
+    const uint8_t *k_pool;
+    const uint8_t *v_pool;
+    const int32_t *cu_q_lens;
+    const int32_t *context_lens;
+    const int32_t *block_tables;
+    void *out;
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t q_heads;
+    int32_t kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t max_q_len;
+    float qk_scale;          // k_scale * sm_scale * log2(e)
+    float v_scale;
+    int32_t out_bf16;
+};
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+}  // namespace kvf8

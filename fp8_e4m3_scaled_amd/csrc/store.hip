@@ -1,0 +1,129 @@
+// kv_store_fp8: quantize new bf16 K/V rows to E4M3 codes and scatter them
+// into the paged pools by slot.
+//
+// [P1, llama-graph.cpp build_attn_scale_kv_inputs]: the cache holds K/s_k and
+// V/s_v; here y = fl32(x * fl32(1/s)) and code = saturating RNE E4M3 of y
+// [P2, ggml_fp32_to_f8_e4m3].
+//
+// One workgroup handles four consecutive input tokens.  Each thread reads a
+// 16-byte-aligned run of bf16 values (coalesced across the workgroup) and
+// writes whole 16-byte runs of codes:
+//   K: 16 consecutive dims of one token lie inside one column quarter of the
+//      tile, which is contiguous in the layout -> one 16-byte store;
+//   V: when the four tokens fill one aligned 4-token group of a block (the
+//      common case of prefill and fills), four dims x four tokens are 16
+//      consecutive bytes -> one 16-byte store.  Otherwise each token's V byte
+//      is written on its own (the decode-step case of one token per sequence).
+
+#include "fp8_device.hpp"
+#include "internal.hpp"
+
+namespace kvf8 {
+namespace {
+
+constexpr int kStoreThreads = 256;
+
+__device__ __forceinline__ uint4 load16(const uint16_t *p) {
+    return *reinterpret_cast<const uint4 *>(p);
+}
+
+__global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a) {
+    const int64_t tok0 = (int64_t)blockIdx.x * 4;
+    const int D = a.head_dim;
+    const int H = a.kv_heads;
+    const int BS = a.block_size;
+    const int quarter = D >> 2;
+    const int64_t tile = (int64_t)BS * D;
+
+    int64_t slot[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) slot[k] = (tok0 + k < a.num_tokens) ? a.slots[tok0 + k] : -1;
+
+    // ---------------- K: items = 4 tokens x H heads x D/16 runs of 16 dims
+    const int runs = D >> 4;
+    const int k_items = 4 * H * runs;
+    for (int it = threadIdx.x; it < k_items; it += kStoreThreads) {
+        const int k = it / (H * runs);
+        const int rem = it - k * (H * runs);
+        const int h = rem / runs;
+        const int r = rem - h * runs;
+        const int64_t s = slot[k];
+        if (s < 0) continue;
+        const uint16_t *src = a.k + (tok0 + k) * a.k_stride + (int64_t)h * D + r * 16;
+        const uint4 lo = load16(src), hi = load16(src + 8);
+        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        uint32_t out[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t p = w[2 * j], q = w[2 * j + 1];
+            out[j] = encode4(scaled(p & 0xFFFF, a.k_inv), scaled(p >> 16, a.k_inv),
+                             scaled(q & 0xFFFF, a.k_inv), scaled(q >> 16, a.k_inv));
+        }
+        const int64_t blk = s / BS;
+        const int t = (int)(s - blk * BS);
+        const int d0 = r * 16;
+        const int64_t off = (blk * H + h) * tile + ((int64_t)(d0 / quarter) * BS + t) * quarter + d0 % quarter;
+        *reinterpret_cast<uint4 *>(a.k_pool + off) = make_uint4(out[0], out[1], out[2], out[3]);
+    }
+
+    // ---------------- V
+    const bool group = slot[0] >= 0 && (slot[0] & 3) == 0 && slot[1] == slot[0] + 1 &&
+                       slot[2] == slot[0] + 2 && slot[3] == slot[0] + 3;
+    const int quads = D >> 2;
+    if (group) {
+        // items = H heads x D/4 runs of 4 dims; each writes 4 dims x 4 tokens
+        const int64_t blk = slot[0] / BS;
+        const int t0 = (int)(slot[0] - blk * BS);
+        for (int it = threadIdx.x; it < H * quads; it += kStoreThreads) {
+            const int h = it / quads;
+            const int d4 = it - h * quads;
+            float y[4][4];   // [token][dim]
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint2 w = *reinterpret_cast<const uint2 *>(a.v + (tok0 + k) * a.v_stride +
+                                                                 (int64_t)h * D + d4 * 4);
+                y[k][0] = scaled(w.x & 0xFFFF, a.v_inv);
+                y[k][1] = scaled(w.x >> 16, a.v_inv);
+                y[k][2] = scaled(w.y & 0xFFFF, a.v_inv);
+                y[k][3] = scaled(w.y >> 16, a.v_inv);
+            }
+            uint32_t out[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) out[j] = encode4(y[0][j], y[1][j], y[2][j], y[3][j]);
+            const int64_t off = (blk * H + h) * tile + ((int64_t)(t0 >> 2) * D + d4 * 4) * 4;
+            *reinterpret_cast<uint4 *>(a.v_pool + off) = make_uint4(out[0], out[1], out[2], out[3]);
+        }
+    } else {
+        // items = 4 tokens x H heads x D/4 runs of 4 dims; bytes at stride 4
+        for (int it = threadIdx.x; it < 4 * H * quads; it += kStoreThreads) {
+            const int k = it / (H * quads);
+            const int rem = it - k * (H * quads);
+            const int h = rem / quads;
+            const int d4 = rem - h * quads;
+            const int64_t s = slot[k];
+            if (s < 0) continue;
+            const uint2 w = *reinterpret_cast<const uint2 *>(a.v + (tok0 + k) * a.v_stride +
+                                                             (int64_t)h * D + d4 * 4);
+            const uint32_t c = encode4(scaled(w.x & 0xFFFF, a.v_inv), scaled(w.x >> 16, a.v_inv),
+                                       scaled(w.y & 0xFFFF, a.v_inv), scaled(w.y >> 16, a.v_inv));
+            const int64_t blk = s / BS;
+            const int t = (int)(s - blk * BS);
+            uint8_t *dst = a.v_pool + (blk * H + h) * tile + ((int64_t)(t >> 2) * D + d4 * 4) * 4 + (t & 3);
+            dst[0] = (uint8_t)(c & 0xFF);
+            dst[4] = (uint8_t)((c >> 8) & 0xFF);
+            dst[8] = (uint8_t)((c >> 16) & 0xFF);
+            dst[12] = (uint8_t)(c >> 24);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_store(const StoreArgs &a, hipStream_t stream) {
+    const int64_t groups = (a.num_tokens + 3) / 4;
+    if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(store_kernel, dim3((unsigned)groups), dim3(kStoreThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace kvf8

@@ -1,0 +1,209 @@
+"""Host-side tests of the C ABI: the library loads, exports every declared
+symbol, and every host-only path (scale intake, shape checks, the block
+allocator, argument checks that fail before any launch) behaves as
+include/kvfp8.h states.  No call here touches a GPU: pools are borrowed
+placeholder addresses that are never dereferenced, and every compute call
+made is one that fails its host-side checks.
+"""
+import ctypes
+import math
+import os
+import re
+import struct
+
+import pytest
+
+import fp8_e4m3_scaled_amd as kv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvfp8.h")
+FAKE_K, FAKE_V = 1 << 40, 2 << 40      # borrowed placeholder "device" addresses
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", text)) - {"sizeof"})
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 17
+    lib = ctypes.CDLL(kv.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(kv.SIGNATURES), "binding and header disagree"
+
+
+def test_version_string():
+    assert "gfx950" in kv.kvf8_version()
+
+
+@pytest.mark.parametrize("bs,h,d", [(16, 2, 64), (16, 8, 128), (32, 2, 256), (32, 8, 128)])
+def test_bytes_per_block_halved(bs, h, d):
+    fp8 = kv.kv_bytes_per_block(bs, h, d, 1)
+    assert fp8 == 2 * bs * h * d
+    assert 2 * fp8 == kv.kv_bytes_per_block(bs, h, d, 2)
+    assert kv.kv_bytes_per_block(0, h, d, 1) == 0 and kv.kv_bytes_per_block(bs, h, d, -1) == 0
+
+
+def _cache(layers=2, nb=64, bs=16, h=2, d=64, ks=None, vs=None, dtype=kv.DTYPE_F32):
+    return kv.kv_cache_alloc(layers, nb, bs, h, d, ks, vs, dtype, FAKE_K, FAKE_V)
+
+
+def test_scales_default_to_one_and_pools_are_borrowed():
+    c = _cache()
+    try:
+        assert kv.kv_cache_get_scales(c, 0) == (1.0, 1.0)
+        k, v, n = kv.kv_cache_pools(c, 1)
+        assert n == 64 * 2 * 16 * 64
+        assert k == FAKE_K + n and v == FAKE_V + n
+    finally:
+        kv.kv_cache_free(c)
+
+
+def test_bf16_scales_widen_exactly():
+    # 0x3CA3 is bf16(0.02) = 0.019958...; 0x3C75 ~ 0.01495
+    c = _cache(ks=[0x3CA3, 0x4000], vs=[0x3C75, 0xBE00], dtype=kv.DTYPE_BF16)
+    try:
+        k0, v0 = kv.kv_cache_get_scales(c, 0)
+        assert struct.unpack("<I", struct.pack("<f", k0))[0] == 0x3CA30000
+        assert struct.unpack("<I", struct.pack("<f", v0))[0] == 0x3C750000
+        assert kv.kv_cache_get_scales(c, 1) == (2.0, -0.125)   # negative scales are allowed
+    finally:
+        kv.kv_cache_free(c)
+
+
+@pytest.mark.parametrize("bad", [0.0, -0.0, math.inf, -math.inf, math.nan, 1e-45, 2.0 ** -129])
+def test_bad_scales_rejected(bad):
+    with pytest.raises(kv.KvF8Error) as ei:
+        _cache(ks=[0.5, bad], vs=[0.5, 0.5])
+    assert ei.value.status == kv.E_SCALE
+    assert "layer 1 (K)" in str(ei.value)
+    with pytest.raises(kv.KvF8Error) as ei:
+        _cache(ks=[0.5, 0.5], vs=[bad, 0.5])
+    assert ei.value.status == kv.E_SCALE and "layer 0 (V)" in str(ei.value)
+
+
+def test_bad_bf16_scale_patterns_rejected():
+    for bits in [0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0x0001]:   # 0, -0, inf, -inf, nan, subnormal
+        with pytest.raises(kv.KvF8Error) as ei:
+            _cache(ks=[0x3F80, bits], vs=[0x3F80, 0x3F80], dtype=kv.DTYPE_BF16)
+        assert ei.value.status == kv.E_SCALE
+
+
+def test_set_scales_checks_and_keeps_old_on_error():
+    c = _cache(ks=[0.5, 0.5], vs=[0.25, 0.25])
+    try:
+        kv.kv_cache_set_scales(c, 1, 0.03, None)
+        assert kv.kv_cache_get_scales(c, 1) == (pytest.approx(0.03), 0.25)
+        with pytest.raises(kv.KvF8Error) as ei:
+            kv.kv_cache_set_scales(c, 1, 0.125, math.nan)
+        assert ei.value.status == kv.E_SCALE
+        assert kv.kv_cache_get_scales(c, 1) == (pytest.approx(0.03), 0.25)
+        with pytest.raises(kv.KvF8Error) as ei:
+            kv.kv_cache_set_scales(c, 2, 0.1, 0.1)
+        assert ei.value.status == kv.E_INVALID
+    finally:
+        kv.kv_cache_free(c)
+
+
+@pytest.mark.parametrize("args", [
+    (0, 64, 16, 2, 64), (1, 0, 16, 2, 64), (1, 64, 16, 0, 64), (1, 64, 8, 2, 64),
+    (1, 64, 64, 2, 64), (1, 64, 16, 2, 96), (1, 64, 16, 2, 512), (1, 1 << 31, 16, 2, 64)])
+def test_bad_shapes_rejected(args):
+    with pytest.raises(kv.KvF8Error) as ei:
+        kv.kv_cache_alloc(*args, None, None, kv.DTYPE_F32, FAKE_K, FAKE_V)
+    assert ei.value.status == kv.E_INVALID
+
+
+def test_mixed_pool_ownership_rejected():
+    with pytest.raises(kv.KvF8Error) as ei:
+        kv.kv_cache_alloc(1, 64, 16, 2, 64, None, None, kv.DTYPE_F32, FAKE_K, None)
+    assert ei.value.status == kv.E_INVALID
+
+
+def test_allocator_lifo_all_or_nothing_and_double_free():
+    c = _cache(nb=8)
+    try:
+        assert kv.kv_blocks_free(c) == 8
+        a = kv.kv_block_alloc(c, 3)
+        assert a == [0, 1, 2]
+        with pytest.raises(kv.KvF8Error) as ei:
+            kv.kv_block_alloc(c, 6)
+        assert ei.value.status == kv.E_NOBLOCKS
+        assert kv.kv_blocks_free(c) == 5          # nothing taken by the failed call
+        kv.kv_block_free(c, [1])
+        assert kv.kv_block_alloc(c, 1) == [1]     # last freed, first out
+        for bad in ([1, 1], [7], [-1], [8]):
+            with pytest.raises(kv.KvF8Error) as ei:
+                kv.kv_block_free(c, bad)
+            assert ei.value.status == kv.E_INVALID
+        assert kv.kv_blocks_free(c) == 5          # failed frees returned nothing
+        kv.kv_block_free(c, a)
+        assert kv.kv_blocks_free(c) == 8
+    finally:
+        kv.kv_cache_free(c)
+
+
+def test_allocator_shuffle_is_seeded_permutation():
+    outs = []
+    for seed in (7, 7, 8):
+        c = _cache(nb=1000)
+        kv.kv_block_shuffle(c, seed)
+        outs.append(kv.kv_block_alloc(c, 1000))
+        kv.kv_cache_free(c)
+    assert outs[0] == outs[1] != outs[2]
+    assert sorted(outs[0]) == list(range(1000)) and outs[0] != list(range(1000))
+
+
+def test_compute_calls_fail_their_host_checks():
+    c = _cache(h=2, d=64)
+    try:
+        def dec(**kw):
+            a = dict(cache=c, layer=0, q_bf16=1 << 30, num_q_heads=4, block_tables=1 << 30,
+                     max_blocks_per_seq=4, seq_lens=1 << 30, num_seqs=2, max_seq_len=64,
+                     sm_scale=0.125, out=1 << 30, out_dtype=kv.DTYPE_F32, stream=0)
+            a.update(kw)
+            with pytest.raises(kv.KvF8Error) as ei:
+                kv.paged_attn_decode(**a)
+            return ei.value.status
+        assert dec(num_q_heads=3) == kv.E_INVALID                  # Hq % Hkv
+        assert dec(num_q_heads=34) == kv.E_UNSUPPORTED              # group of 17
+        assert dec(sm_scale=0.0) == kv.E_INVALID
+        assert dec(sm_scale=math.nan) == kv.E_INVALID
+        assert dec(layer=2) == kv.E_INVALID
+        assert dec(max_seq_len=65) == kv.E_INVALID                 # beyond the table
+        assert dec(out_dtype=7) == kv.E_INVALID
+        assert dec(q_bf16=(1 << 30) + 2) == kv.E_INVALID            # misaligned q
+        with pytest.raises(kv.KvF8Error) as ei:
+            kv.kv_store_fp8(c, 0, 1 << 30, 1 << 30, 64, 128, 1 << 30, 4, 0)   # stride < H*D
+        assert ei.value.status == kv.E_INVALID
+        with pytest.raises(kv.KvF8Error) as ei:
+            kv.kv_store_fp8(c, 0, None, 1 << 30, 128, 128, 1 << 30, 4, 0)
+        assert ei.value.status == kv.E_INVALID
+        kv.kv_store_fp8(c, 0, None, None, 128, 128, None, 0, 0)     # zero tokens: no-op
+        for rot in (0, 3, 66):
+            with pytest.raises(kv.KvF8Error) as ei:
+                kv.kv_shift_rope(c, 0, 1 << 30, 4, -1, 1e4, rot, kv.ROPE_NEOX, 0)
+            assert ei.value.status == kv.E_INVALID
+        with pytest.raises(kv.KvF8Error) as ei:
+            kv.kv_shift_rope(c, 0, 1 << 30, 4, -1, -1.0, 64, kv.ROPE_NEOX, 0)
+        assert ei.value.status == kv.E_INVALID
+        with pytest.raises(kv.KvF8Error) as ei:
+            kv.paged_attn_prefill_chunk(c, 0, 1 << 30, 5, 1 << 30, 1 << 30, 1 << 30, 4, 1, 8, 8,
+                                        16, 0.125, 1 << 30, kv.DTYPE_F32, 0)
+        assert ei.value.status == kv.E_INVALID
+    finally:
+        kv.kv_cache_free(c)
+
+
+def test_workspace_size_is_consistent():
+    c = _cache(h=2, d=64)
+    try:
+        assert kv.paged_attn_decode_workspace(c, 0, 4, 64) == 0
+        for L in (1, 64, 100000):
+            n = kv.paged_attn_decode_workspace(c, 4, 4, L)
+            assert n >= 0 and n % 4 == 0
+    finally:
+        kv.kv_cache_free(c)
