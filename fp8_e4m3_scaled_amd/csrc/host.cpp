@@ -377,6 +377,7 @@ kvf8_status paged_attn_decode(kvf8_cache *c, int32_t layer, const uint16_t *q_bf
     a.seq_lens = seq_lens;
     a.out = out;
     a.partials = need > 0 ? static_cast<float *>(workspace) : nullptr;
+    a.num_blocks = c->num_blocks;
     a.max_blocks = max_blocks_per_seq;
     a.num_seqs = num_seqs;
     a.q_heads = num_q_heads;
@@ -427,6 +428,7 @@ kvf8_status paged_attn_prefill_chunk(kvf8_cache *c, int32_t layer, const uint16_
     a.context_lens = context_lens;
     a.block_tables = block_tables;
     a.out = out;
+    a.num_blocks = c->num_blocks;
     a.max_blocks = max_blocks_per_seq;
     a.num_seqs = num_seqs;
     a.q_heads = num_q_heads;

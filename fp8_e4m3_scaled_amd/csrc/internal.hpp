@@ -52,6 +52,7 @@ struct DecodeArgs {
     const int32_t *seq_lens;
     void *out;
     float *partials;         // [num_seqs][q_heads][splits][head_dim + 2] or null
+    int64_t num_blocks;      // pool blocks; table entries are clamped below it
     int32_t max_blocks;
     int32_t num_seqs;
     int32_t q_heads;
@@ -93,6 +94,7 @@ struct PrefillArgs {
     const int32_t *context_lens;
     const int32_t *block_tables;
     void *out;
+    int64_t num_blocks;
     int32_t max_blocks;
     int32_t num_seqs;
     int32_t q_heads;
