@@ -27,6 +27,9 @@ CFLAGS = [
     "-Wall", "-Wextra", "-Wno-unused-parameter",
     # packed FP32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators stay in ordinary VGPRs: the softmax rescales them
+    # with VALU ops, and AGPR-resident accumulators would be copied every step
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -19,8 +19,9 @@
 //     is exactly the B operand of the next product;
 //   * O^T[d][head] += V^T P^T on v_mfma_f32_16x16x32_f16 (codes -> f16 exact,
 //     P in f16), over 32 tokens per instruction;
-//   * the online softmax runs in the log2 domain: running max per head,
-//     per-lane partial sums, a rescale of the accumulators when the max moves.
+//   * the online softmax runs in the log2 domain against a per-head reference
+//     max that only moves when a score exceeds it by more than 2^8 (lazy
+//     rescale), with per-lane partial sums.
 // The next step's K/V bytes and block ids are loaded before the current step
 // is computed.  The four waves then combine through LDS; with one split the
 // workgroup writes the output, otherwise it writes (max, sum, acc) partials
@@ -37,6 +38,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStep = 32;                 // tokens per wave step
+constexpr float kLazy = 8.0f;             // log2 headroom of the lazy softmax reference
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -54,46 +56,162 @@ __device__ __forceinline__ void store_out(void *out, int64_t idx, float v, int b
 
 template <int D>
 struct StepRegs {
-    static constexpr int NW = D / 16;     // dwords per lane per tile (K and V each)
-    uint32_t k[2][NW];
-    uint32_t v[2][NW];
+    static constexpr int NQ = D / 64;     // 16-byte loads per lane per tile (K and V each)
+    u32x4 k[2][NQ];
+    u32x4 v[2][NQ];
+    __device__ __forceinline__ uint32_t kw(int t, int j) const { return k[t][j >> 2][j & 3]; }
+    __device__ __forceinline__ uint32_t vw(int t, int j) const { return v[t][j >> 2][j & 3]; }
 };
 
+// Loads of the K/V ring are issued as plain global_load_dwordx4 and waited for
+// explicitly (below): the compiler's own wait placement cannot see through the
+// ring and would drain every outstanding load at the loop head.
+__device__ __forceinline__ void gload16(u32x4 &dst, const void *p) {
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst) : "v"(p) : "memory");
+}
+
+// Wait until at most N vector-memory loads are outstanding, then hand the
+// step's registers on: every register of the buffer is an operand of the
+// wait, so no use of it can be scheduled before the wait.
+template <int N, int D>
+__device__ __forceinline__ void wait_step(StepRegs<D> &r) {
+    asm volatile("s_waitcnt vmcnt(%1)" : "+v"(r.k[0][0]) : "n"(N) : "memory");
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < StepRegs<D>::NQ; ++i) {
+            asm volatile("" : "+v"(r.k[t][i]));
+            asm volatile("" : "+v"(r.v[t][i]));
+        }
+}
+
+// Issue the loads of one 32-token step: per lane, D/64 16-byte loads of K and
+// D/64 of V for each of the two 16-token tiles.  blk0 / blk1 are the pool
+// blocks of the two tiles.  A step past the wave's end (live == false) keeps
+// the same number of loads but points every lane at one shared 16-byte line,
+// so the ring stays branch-free without moving extra bytes.
 template <int D, int BS>
 __device__ __forceinline__ void load_step(StepRegs<D> &r, const uint8_t *k_pool, const uint8_t *v_pool,
-                                          const int32_t *table, uint32_t last_block, int kv_heads, int kvh,
-                                          int p, int end, int m, int g) {
+                                          uint32_t blk0, uint32_t blk1, int kv_heads, int kvh, int p,
+                                          int m, int g, bool live) {
     constexpr int Q4 = D / 4;
-    constexpr int NW = D / 16;
+    constexpr int NQ = D / 64;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const int pt = p + 16 * t;
-        if (pt < end) {
-            // a block id outside the pool is a caller error; clamp it so it cannot fault
-            const uint32_t blk = min((uint32_t)table[pt / BS], last_block);
-            const int tb = pt % BS;
-            const int64_t base = ((int64_t)blk * kv_heads + kvh) * (BS * D);
-            const u32x4 *kp = reinterpret_cast<const u32x4 *>(k_pool + base + (g * BS + tb + m) * Q4);
-            const u32x4 *vp = reinterpret_cast<const u32x4 *>(v_pool + base + ((tb / 4 + g) * D + (D / 16) * m) * 4);
+        const uint32_t blk = t == 0 ? blk0 : blk1;
+        const int tb = (p + 16 * t) % BS;
+        const int64_t base = ((int64_t)blk * kv_heads + kvh) * (BS * D);
+        const uint8_t *kp = live ? k_pool + base + (g * BS + tb + m) * Q4 : k_pool;
+        const uint8_t *vp = live ? v_pool + base + ((tb / 4 + g) * D + (D / 16) * m) * 4 : k_pool;
+        const int inc = live ? 16 : 0;
 #pragma unroll
-            for (int i = 0; i < NW / 4; ++i) {
-                const u32x4 kq = __builtin_nontemporal_load(kp + i);
-                const u32x4 vq = __builtin_nontemporal_load(vp + i);
-                r.k[t][4 * i + 0] = kq.x; r.k[t][4 * i + 1] = kq.y; r.k[t][4 * i + 2] = kq.z; r.k[t][4 * i + 3] = kq.w;
-                r.v[t][4 * i + 0] = vq.x; r.v[t][4 * i + 1] = vq.y; r.v[t][4 * i + 2] = vq.z; r.v[t][4 * i + 3] = vq.w;
-            }
-        } else {
+        for (int i = 0; i < NQ; ++i) gload16(r.k[t][i], kp + inc * i);
 #pragma unroll
-            for (int i = 0; i < NW; ++i) { r.k[t][i] = 0; r.v[t][i] = 0; }
-        }
+        for (int i = 0; i < NQ; ++i) gload16(r.v[t][i], vp + inc * i);
     }
 }
 
+// Online-softmax state of one wave: the O^T accumulators of its lane and the
+// running max / partial sum of its head column.
+template <int D>
+struct SoftmaxState {
+    f32x4 acc[D / 16];
+    float run_max;
+    float run_sum;
+};
+
+// One 32-token step of one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void compute_step(SoftmaxState<D> &st, StepRegs<D> &cur, const bf16x8 *qb,
+                                             int p, int c1, int g, float qk_scale) {
+    constexpr int KK = D / 32;
+    constexpr int MT = D / 16;
+    // ---- S^T = K Q^T for the two tiles
+    f32x4 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const uint32_t w0 = cur.kw(t, 2 * kk), w1 = cur.kw(t, 2 * kk + 1);
+            const bf16x2 e0 = codes_to_bf16x2<false>(w0), e1 = codes_to_bf16x2<true>(w0);
+            const bf16x2 e2 = codes_to_bf16x2<false>(w1), e3 = codes_to_bf16x2<true>(w1);
+            const bf16x8 ka = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+            s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[kk], s[t], 0, 0, 0);
+        }
+    }
+
+    // ---- scale into the log2 domain; only the last step of a chunk has tokens to mask
+    const bool tail = p + kStep > c1;      // the same for the whole wave
+    float x[8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[4 * t + i] = s[t][i] * qk_scale;
+    if (tail) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (p + 16 * t + 4 * g + i >= c1) x[4 * t + i] = -__builtin_inff();
+    }
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // Lazy rescale: probabilities are taken relative to a per-head reference
+    // that only moves when a score exceeds it by more than 2^kLazy, so P stays
+    // <= 2^kLazy (well inside f16) and the accumulators are rescaled rarely.
+    // The result is unchanged: the final normalization uses the same reference.
+    if (__any(mx > st.run_max + kLazy)) {
+        const float new_ref = fmaxf(st.run_max, mx);
+        const float alpha = __builtin_amdgcn_exp2f(st.run_max - new_ref);   // 0 on the first step
+        st.run_sum *= alpha;
+#pragma unroll
+        for (int j = 0; j < MT; ++j) st.acc[j] *= alpha;
+        st.run_max = new_ref;
+    }
+    float pr[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(x[i] - st.run_max);
+        psum += pr[i];
+    }
+    st.run_sum += psum;
+
+    // ---- tail: codes of tokens past the end must not reach the product (NaN * 0)
+    if (tail) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int valid = c1 - (p + 16 * t + 4 * g);          // tokens of this lane's group left
+            const uint32_t keep = valid >= 4 ? 0xFFFFFFFFu : valid <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * valid));
+#pragma unroll
+            for (int i = 0; i < StepRegs<D>::NQ; ++i) cur.v[t][i] &= keep;
+        }
+    }
+
+    // ---- O^T += V^T P^T
+    const f16x8 pb = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3],
+                      (_Float16)pr[4], (_Float16)pr[5], (_Float16)pr[6], (_Float16)pr[7]};
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+        const f16x2 e0 = codes_to_f16x2<false>(cur.vw(0, j)), e1 = codes_to_f16x2<true>(cur.vw(0, j));
+        const f16x2 e2 = codes_to_f16x2<false>(cur.vw(1, j)), e3 = codes_to_f16x2<true>(cur.vw(1, j));
+        const f16x8 va = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+        st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, st.acc[j], 0, 0, 0);
+    }
+}
+
+// Register buffers in flight per wave: the step being computed plus
+// (NBUF - 1) steps whose loads are outstanding.
+template <int D>
+struct Depth { static constexpr int NBUF = D >= 256 ? 2 : 3; };
+
 template <int D, int BS>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
-    constexpr int NW = D / 16;     // dwords of K (and of V) per lane per tile
     constexpr int KK = D / 32;     // QK^T instructions per tile
     constexpr int MT = D / 16;     // PV instructions per step (one per 16 dims)
+    constexpr int NBUF = Depth<D>::NBUF;
 
     extern __shared__ float smem[];   // [waves][G] max, [waves][G] sum, [waves][G][D] acc
 
@@ -135,88 +253,62 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         }
     }
 
+    // Block ids of this wave's tiles, one per lane: tile j of the wave is step
+    // j/2, half j%2, at position c0 + 32*wave + 128*(j/2) + 16*(j%2).  A chunk
+    // holds at most 32 steps per wave, so 64 lanes cover it.  Positions past
+    // the sequence read its last block (never used unmasked).
     const int32_t *table = a.block_tables + (int64_t)b * a.max_blocks;
-    f32x4 acc[MT];
+    uint32_t ids;
+    {
+        const int pos = c0 + kStep * wave + kStep * kWaves * (lane >> 1) + 16 * (lane & 1);
+        const int e = min(pos, L - 1) / BS;
+        ids = min((uint32_t)table[e], last_block);   // an id outside the pool is clamped
+    }
+    // Q and the ids must have landed before the load ring starts, so that the
+    // waits inside the ring only count ring loads.
+    __builtin_amdgcn_s_waitcnt(0);
+
+    SoftmaxState<D> st;
 #pragma unroll
-    for (int j = 0; j < MT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float run_max = -__builtin_inff();
-    float run_sum = 0.0f;
+    for (int j = 0; j < MT; ++j) st.acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.run_max = -__builtin_inff();
+    st.run_sum = 0.0f;
 
     const int stride = kStep * kWaves;
-    int p = c0 + kStep * wave;
-    StepRegs<D> cur, nxt;
-    if (p < c1) load_step<D, BS>(cur, a.k_pool, a.v_pool, table, last_block, a.kv_heads, kvh, p, c1, m, g);
-
-    for (; p < c1; p += stride) {
-        const int pn = p + stride;
-        if (pn < c1) load_step<D, BS>(nxt, a.k_pool, a.v_pool, table, last_block, a.kv_heads, kvh, pn, c1, m, g);
-
-        // ---- S^T = K Q^T for the two tiles
-        f32x4 s[2];
+    const int nsteps = c1 > c0 + kStep * wave ? (c1 - c0 - kStep * wave + stride - 1) / stride : 0;
+    const int p0 = c0 + kStep * wave;
+    constexpr int LOADS = 4 * StepRegs<D>::NQ;      // loads per step
+    auto issue = [&](StepRegs<D> &r, int i) {
+        const bool live = i < nsteps;
+        const int ii = live ? i : 0;
+        const uint32_t b0 = __builtin_amdgcn_readlane(ids, 2 * ii);
+        const uint32_t b1 = __builtin_amdgcn_readlane(ids, 2 * ii + 1);
+        load_step<D, BS>(r, a.k_pool, a.v_pool, b0, b1, a.kv_heads, kvh, p0 + ii * stride, m, g, live);
+    };
+    StepRegs<D> buf[NBUF];
+    if (nsteps > 0) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const uint32_t w0 = cur.k[t][2 * kk], w1 = cur.k[t][2 * kk + 1];
-                const bf16x2 e0 = codes_to_bf16x2<false>(w0), e1 = codes_to_bf16x2<true>(w0);
-                const bf16x2 e2 = codes_to_bf16x2<false>(w1), e3 = codes_to_bf16x2<true>(w1);
-                const bf16x8 ka = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
-                s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[kk], s[t], 0, 0, 0);
-            }
-        }
-
-        // ---- scale into the log2 domain, mask tokens past the chunk end
-        float x[8];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = p + 16 * t + 4 * g + i;
-                x[4 * t + i] = tok < c1 ? s[t][i] * a.qk_scale : -__builtin_inff();
-            }
-        float mx = x[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float new_max = fmaxf(run_max, mx);
-        const float alpha = exp2f(run_max - new_max);
-        float pr[8];
-        float psum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            pr[i] = exp2f(x[i] - new_max);
-            psum += pr[i];
-        }
-        run_sum = run_sum * alpha + psum;
-        run_max = new_max;
-#pragma unroll
-        for (int j = 0; j < MT; ++j) acc[j] *= alpha;
-
-        // ---- tail: codes of tokens past the end must not reach the product (NaN * 0)
-        if (p + kStep > c1) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int valid = c1 - (p + 16 * t + 4 * g);          // tokens of this lane's group left
-                const uint32_t keep = valid >= 4 ? 0xFFFFFFFFu : valid <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * valid));
-#pragma unroll
-                for (int j = 0; j < NW; ++j) cur.v[t][j] &= keep;
-            }
-        }
-
-        // ---- O^T += V^T P^T
-        const f16x8 pb = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3],
-                          (_Float16)pr[4], (_Float16)pr[5], (_Float16)pr[6], (_Float16)pr[7]};
-#pragma unroll
-        for (int j = 0; j < MT; ++j) {
-            const f16x2 e0 = codes_to_f16x2<false>(cur.v[0][j]), e1 = codes_to_f16x2<true>(cur.v[0][j]);
-            const f16x2 e2 = codes_to_f16x2<false>(cur.v[1][j]), e3 = codes_to_f16x2<true>(cur.v[1][j]);
-            const f16x8 va = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[j], 0, 0, 0);
-        }
-        if (pn < c1) cur = nxt;
+        for (int i = 0; i < NBUF - 1; ++i) issue(buf[i], i);
     }
+    for (int i = 0; i < nsteps; i += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+            const int step = i + u;
+            if (step >= nsteps) break;
+            // keep the next NBUF-1 steps' loads in flight while this one computes
+            issue(buf[(u + NBUF - 1) % NBUF], step + NBUF - 1);
+            wait_step<LOADS * (NBUF - 1)>(buf[u]);
+            compute_step<D>(st, buf[u], qb, p0 + step * stride, c1, g, a.qk_scale);
+        }
+    }
+    // Drain the ring.  The wait names every ring register, so none of them can
+    // be reused for anything else while a (possibly dummy) load into it is still
+    // in flight.
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) wait_step<0>(buf[u]);
+    f32x4 *acc = st.acc;
+    float run_max = st.run_max;
+    float run_sum = st.run_sum;
 
     // ---- combine the four waves
     run_sum += __shfl_xor(run_sum, 16);
@@ -312,7 +404,8 @@ int env_int(const char *name, int dflt) {
 // multiple of one round of wave steps.
 void decode_plan(int32_t num_seqs, int32_t kv_heads, int32_t head_dim, int32_t block_size,
                  int32_t max_seq_len, int32_t *splits, int32_t *chunk_tokens) {
-    static const int max_chunk = env_int("KVF8_DECODE_MAX_CHUNK", 4096);
+    // a wave holds the block ids of at most 64 tiles (32 steps): chunk <= 4096 tokens
+    static const int max_chunk = min(env_int("KVF8_DECODE_MAX_CHUNK", 4096), 32 * kStep * kWaves);
     static const int target_wgs = env_int("KVF8_DECODE_TARGET_WGS", 512);
     const int round = kStep * kWaves;
     const int64_t pairs = (int64_t)num_seqs * kv_heads;
@@ -325,6 +418,7 @@ void decode_plan(int32_t num_seqs, int32_t kv_heads, int32_t head_dim, int32_t b
     int64_t chunk = (max_seq_len + s - 1) / s;
     chunk = ((chunk + round - 1) / round) * round;
     if (chunk < round) chunk = round;
+    if (chunk > max_chunk) chunk = max_chunk;
     s = (max_seq_len + chunk - 1) / chunk;
     if (s < 1) s = 1;
     *splits = (int32_t)s;

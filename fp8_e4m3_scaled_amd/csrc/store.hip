@@ -22,97 +22,103 @@ namespace kvf8 {
 namespace {
 
 constexpr int kStoreThreads = 256;
-
-__device__ __forceinline__ uint4 load16(const uint16_t *p) {
-    return *reinterpret_cast<const uint4 *>(p);
-}
+constexpr int kGroups = 1;          // four-token groups per workgroup
 
 __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a) {
-    const int64_t tok0 = (int64_t)blockIdx.x * 4;
     const int D = a.head_dim;
     const int H = a.kv_heads;
     const int BS = a.block_size;
     const int quarter = D >> 2;
     const int64_t tile = (int64_t)BS * D;
+    const uint16_t *__restrict__ kin = a.k;
+    const uint16_t *__restrict__ vin = a.v;
+    uint8_t *__restrict__ kout = a.k_pool;
+    uint8_t *__restrict__ vout = a.v_pool;
+    const int runs = D >> 4;            // 16-dim runs per head
+    const int quads = D >> 2;           // 4-dim runs per head
+    const int k_items = 4 * H * runs;   // per group: 4 tokens x H heads x runs
+    const int v_items = H * quads;      // per group (four-token path)
 
-    int64_t slot[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) slot[k] = (tok0 + k < a.num_tokens) ? a.slots[tok0 + k] : -1;
+    for (int grp = 0; grp < kGroups; ++grp) {
+        const int64_t tok0 = ((int64_t)blockIdx.x * kGroups + grp) * 4;
+        if (tok0 >= a.num_tokens) break;
+        int64_t slot[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) slot[k] = (tok0 + k < a.num_tokens) ? a.slots[tok0 + k] : -1;
 
-    // ---------------- K: items = 4 tokens x H heads x D/16 runs of 16 dims
-    const int runs = D >> 4;
-    const int k_items = 4 * H * runs;
-    for (int it = threadIdx.x; it < k_items; it += kStoreThreads) {
-        const int k = it / (H * runs);
-        const int rem = it - k * (H * runs);
-        const int h = rem / runs;
-        const int r = rem - h * runs;
-        const int64_t s = slot[k];
-        if (s < 0) continue;
-        const uint16_t *src = a.k + (tok0 + k) * a.k_stride + (int64_t)h * D + r * 16;
-        const uint4 lo = load16(src), hi = load16(src + 8);
-        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        uint32_t out[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t p = w[2 * j], q = w[2 * j + 1];
-            out[j] = encode4(scaled(p & 0xFFFF, a.k_inv), scaled(p >> 16, a.k_inv),
-                             scaled(q & 0xFFFF, a.k_inv), scaled(q >> 16, a.k_inv));
-        }
-        const int64_t blk = s / BS;
-        const int t = (int)(s - blk * BS);
-        const int d0 = r * 16;
-        const int64_t off = (blk * H + h) * tile + ((int64_t)(d0 / quarter) * BS + t) * quarter + d0 % quarter;
-        *reinterpret_cast<uint4 *>(a.k_pool + off) = make_uint4(out[0], out[1], out[2], out[3]);
-    }
-
-    // ---------------- V
-    const bool group = slot[0] >= 0 && (slot[0] & 3) == 0 && slot[1] == slot[0] + 1 &&
-                       slot[2] == slot[0] + 2 && slot[3] == slot[0] + 3;
-    const int quads = D >> 2;
-    if (group) {
-        // items = H heads x D/4 runs of 4 dims; each writes 4 dims x 4 tokens
-        const int64_t blk = slot[0] / BS;
-        const int t0 = (int)(slot[0] - blk * BS);
-        for (int it = threadIdx.x; it < H * quads; it += kStoreThreads) {
-            const int h = it / quads;
-            const int d4 = it - h * quads;
-            float y[4][4];   // [token][dim]
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint2 w = *reinterpret_cast<const uint2 *>(a.v + (tok0 + k) * a.v_stride +
-                                                                 (int64_t)h * D + d4 * 4);
-                y[k][0] = scaled(w.x & 0xFFFF, a.v_inv);
-                y[k][1] = scaled(w.x >> 16, a.v_inv);
-                y[k][2] = scaled(w.y & 0xFFFF, a.v_inv);
-                y[k][3] = scaled(w.y >> 16, a.v_inv);
-            }
-            uint32_t out[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) out[j] = encode4(y[0][j], y[1][j], y[2][j], y[3][j]);
-            const int64_t off = (blk * H + h) * tile + ((int64_t)(t0 >> 2) * D + d4 * 4) * 4;
-            *reinterpret_cast<uint4 *>(a.v_pool + off) = make_uint4(out[0], out[1], out[2], out[3]);
-        }
-    } else {
-        // items = 4 tokens x H heads x D/4 runs of 4 dims; bytes at stride 4
-        for (int it = threadIdx.x; it < 4 * H * quads; it += kStoreThreads) {
-            const int k = it / (H * quads);
-            const int rem = it - k * (H * quads);
-            const int h = rem / quads;
-            const int d4 = rem - h * quads;
+        // ---------------- K: 16 dims of one token -> one 16-byte run of codes
+        for (int it = threadIdx.x; it < k_items; it += kStoreThreads) {
+            const int k = it / (H * runs);
+            const int rem = it - k * (H * runs);
+            const int h = rem / runs;
+            const int r = rem - h * runs;
             const int64_t s = slot[k];
             if (s < 0) continue;
-            const uint2 w = *reinterpret_cast<const uint2 *>(a.v + (tok0 + k) * a.v_stride +
-                                                             (int64_t)h * D + d4 * 4);
-            const uint32_t c = encode4(scaled(w.x & 0xFFFF, a.v_inv), scaled(w.x >> 16, a.v_inv),
-                                       scaled(w.y & 0xFFFF, a.v_inv), scaled(w.y >> 16, a.v_inv));
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(kin + (tok0 + k) * a.k_stride + (int64_t)h * D + r * 16);
+            const u32x4 lo = src[0], hi = src[1];
+            const uint32_t w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            u32x4 out;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t p0 = w[2 * j], p1 = w[2 * j + 1];
+                out[j] = encode4(scaled(p0 & 0xFFFF, a.k_inv), scaled(p0 >> 16, a.k_inv),
+                                 scaled(p1 & 0xFFFF, a.k_inv), scaled(p1 >> 16, a.k_inv));
+            }
             const int64_t blk = s / BS;
             const int t = (int)(s - blk * BS);
-            uint8_t *dst = a.v_pool + (blk * H + h) * tile + ((int64_t)(t >> 2) * D + d4 * 4) * 4 + (t & 3);
-            dst[0] = (uint8_t)(c & 0xFF);
-            dst[4] = (uint8_t)((c >> 8) & 0xFF);
-            dst[8] = (uint8_t)((c >> 16) & 0xFF);
-            dst[12] = (uint8_t)(c >> 24);
+            const int d0 = r * 16;
+            const int64_t off = (blk * H + h) * tile + ((int64_t)(d0 / quarter) * BS + t) * quarter + d0 % quarter;
+            *reinterpret_cast<u32x4 *>(kout + off) = out;
+        }
+
+        // ---------------- V
+        const bool group = slot[0] >= 0 && (slot[0] & 3) == 0 && slot[1] == slot[0] + 1 &&
+                           slot[2] == slot[0] + 2 && slot[3] == slot[0] + 3;
+        if (group) {
+            // four dims x four tokens -> one 16-byte run of codes
+            const int64_t blk = slot[0] / BS;
+            const int t0 = (int)(slot[0] - blk * BS);
+            for (int it = threadIdx.x; it < v_items; it += kStoreThreads) {
+                const int h = it / quads;
+                const int d4 = it - h * quads;
+                float y[4][4];   // [token][dim]
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint2 w = *reinterpret_cast<const uint2 *>(vin + (tok0 + k) * a.v_stride +
+                                                                     (int64_t)h * D + d4 * 4);
+                    y[k][0] = scaled(w.x & 0xFFFF, a.v_inv);
+                    y[k][1] = scaled(w.x >> 16, a.v_inv);
+                    y[k][2] = scaled(w.y & 0xFFFF, a.v_inv);
+                    y[k][3] = scaled(w.y >> 16, a.v_inv);
+                }
+                u32x4 out;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) out[j] = encode4(y[0][j], y[1][j], y[2][j], y[3][j]);
+                const int64_t off = (blk * H + h) * tile + ((int64_t)(t0 >> 2) * D + d4 * 4) * 4;
+                *reinterpret_cast<u32x4 *>(vout + off) = out;
+            }
+        } else {
+            // one token at a time: its four codes sit 4 bytes apart
+            for (int it = threadIdx.x; it < 4 * v_items; it += kStoreThreads) {
+                const int k = it / v_items;
+                const int rem = it - k * v_items;
+                const int h = rem / quads;
+                const int d4 = rem - h * quads;
+                const int64_t s = slot[k];
+                if (s < 0) continue;
+                const uint2 w = *reinterpret_cast<const uint2 *>(vin + (tok0 + k) * a.v_stride +
+                                                                 (int64_t)h * D + d4 * 4);
+                const uint32_t c = encode4(scaled(w.x & 0xFFFF, a.v_inv), scaled(w.x >> 16, a.v_inv),
+                                           scaled(w.y & 0xFFFF, a.v_inv), scaled(w.y >> 16, a.v_inv));
+                const int64_t blk = s / BS;
+                const int t = (int)(s - blk * BS);
+                uint8_t *dst = vout + (blk * H + h) * tile + ((int64_t)(t >> 2) * D + d4 * 4) * 4 + (t & 3);
+                dst[0] = (uint8_t)(c & 0xFF);
+                dst[4] = (uint8_t)((c >> 8) & 0xFF);
+                dst[8] = (uint8_t)((c >> 16) & 0xFF);
+                dst[12] = (uint8_t)(c >> 24);
+            }
         }
     }
 }
@@ -120,9 +126,9 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a) {
 }  // namespace
 
 hipError_t launch_store(const StoreArgs &a, hipStream_t stream) {
-    const int64_t groups = (a.num_tokens + 3) / 4;
-    if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(store_kernel, dim3((unsigned)groups), dim3(kStoreThreads), 0, stream, a);
+    const int64_t wgs = (a.num_tokens + 4 * kGroups - 1) / (4 * kGroups);
+    if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(store_kernel, dim3((unsigned)wgs), dim3(kStoreThreads), 0, stream, a);
     return hipGetLastError();
 }
 

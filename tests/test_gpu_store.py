@@ -73,9 +73,12 @@ def test_store_negative_slots_padding_and_untouched_bytes(BS, Hkv, D):
     NB, T = 9, 37                      # ragged: not a multiple of four tokens
     k = rng.integers(0, 1 << 16, size=(T, Hkv, D), dtype=np.uint16)
     v = rng.integers(0, 1 << 16, size=(T, Hkv, D), dtype=np.uint16)
-    slots = rng.choice(NB * BS, size=T, replace=False).astype(np.int64)
+    group = np.arange(40, 44)                       # one aligned four-token group
+    others = np.setdiff1d(np.arange(NB * BS), group)
+    slots = rng.choice(others, size=T, replace=False).astype(np.int64)   # no repeated slot
+    slots[8:12] = group
     slots[[0, 5, 6, 36]] = -1
-    slots[8:12] = [40, 41, 42, 43]      # one aligned four-token group
+    assert len(set(slots[slots >= 0].tolist())) == int((slots >= 0).sum())
     log(f"store ragged/padded: BS={BS} Hkv={Hkv} D={D}")
     with GpuCache(NB, BS, Hkv, D, 0.07, 0.011, fill=0xA5) as c:
         ks, vs = kv.kv_cache_get_scales(c.handle, 0)
