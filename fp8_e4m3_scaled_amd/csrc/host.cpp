@@ -317,6 +317,7 @@ kvf8_status kv_store_fp8(kvf8_cache *c, int32_t layer, const uint16_t *k_bf16,
     a.v_stride = v_tok_stride;
     a.slots = slot_mapping;
     a.num_tokens = num_tokens;
+    a.pool_slots = c->num_blocks * c->block_size;
     a.k_pool = k_pool_of(c, layer);
     a.v_pool = v_pool_of(c, layer);
     a.k_inv = c->k_inv[layer];
@@ -462,6 +463,7 @@ kvf8_status kv_shift_rope(kvf8_cache *c, int32_t layer, const int64_t *slots, in
     a.k_pool = k_pool_of(c, layer);
     a.slots = slots;
     a.n_slots = n_slots;
+    a.pool_slots = c->num_blocks * c->block_size;
     a.kv_heads = c->kv_heads;
     a.head_dim = c->head_dim;
     a.block_size = c->block_size;

@@ -33,6 +33,7 @@ struct StoreArgs {
     int64_t v_stride;
     const int64_t *slots;
     int64_t num_tokens;
+    int64_t pool_slots;      // num_blocks * block_size: slots at or past it are skipped
     uint8_t *k_pool;         // this layer
     uint8_t *v_pool;
     float k_inv;
@@ -75,6 +76,7 @@ struct KShiftArgs {
     uint8_t *k_pool;
     const int64_t *slots;
     int64_t n_slots;
+    int64_t pool_slots;      // num_blocks * block_size: slots at or past it are skipped
     int32_t kv_heads;
     int32_t head_dim;
     int32_t block_size;

@@ -3,7 +3,6 @@
 
 namespace kvf8 {
 
-hipError_t launch_kshift(const KShiftArgs &, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_prefill(const PrefillArgs &, hipStream_t) { return hipErrorNotSupported; }
 
 }  // namespace kvf8

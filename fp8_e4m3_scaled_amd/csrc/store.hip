@@ -3,7 +3,8 @@
 //
 // [P1, llama-graph.cpp build_attn_scale_kv_inputs]: the cache holds K/s_k and
 // V/s_v; here y = fl32(x * fl32(1/s)) and code = saturating RNE E4M3 of y
-// [P2, ggml_fp32_to_f8_e4m3].
+// [P2, ggml_fp32_to_f8_e4m3].  Negative slots and slots past the pool are
+// skipped.
 //
 // One workgroup handles four consecutive input tokens.  Each thread reads a
 // 16-byte-aligned run of bf16 values (coalesced across the workgroup) and
@@ -45,7 +46,10 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a) {
         if (tok0 >= a.num_tokens) break;
         int64_t slot[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) slot[k] = (tok0 + k < a.num_tokens) ? a.slots[tok0 + k] : -1;
+        for (int k = 0; k < 4; ++k) {
+            slot[k] = (tok0 + k < a.num_tokens) ? a.slots[tok0 + k] : -1;
+            if (slot[k] >= a.pool_slots) slot[k] = -1;    // outside the pool: skipped, never written
+        }
 
         // ---------------- K: 16 dims of one token -> one 16-byte run of codes
         for (int it = threadIdx.x; it < k_items; it += kStoreThreads) {

@@ -159,14 +159,14 @@ kvf8_status kv_block_shuffle(kvf8_cache *cache, uint64_t seed);
  * signed zero follow [P2, ggml_fp32_to_f8_e4m3]: NaN -> sign|0x7F with the
  * input's sign, +-Inf and |y| >= 448 -> sign|0x7E, zero keeps its sign.
  * The division of [P1, build_attn_scale_kv_inputs] (store K/s, V/s) is done
- * as a multiply by the reciprocal.  Slots < 0 are skipped.
+ * as a multiply by the reciprocal.
  *
  * k_bf16, v_bf16 (device): [num_tokens][num_kv_heads][head_dim] bf16 rows;
  *   row i starts at element i * k_tok_stride (resp. v_tok_stride), heads and
  *   dims are contiguous inside a row; stride >= num_kv_heads*head_dim.
- * slot_mapping (device): int64 [num_tokens].  Every slot must be below
- *   num_blocks * block_size and no slot may repeat in one call (the result
- *   of a repeated slot is undefined); neither is checked on the device.
+ * slot_mapping (device): int64 [num_tokens].  Slots < 0 and slots >=
+ *   num_blocks * block_size are skipped (nothing is written for them).  No
+ *   slot may repeat in one call: the bytes of a repeated slot are undefined.
  * num_tokens == 0 is a no-op.
  */
 kvf8_status kv_store_fp8(kvf8_cache *cache, int32_t layer, const uint16_t *k_bf16,
@@ -253,8 +253,8 @@ kvf8_status paged_attn_prefill_chunk(kvf8_cache *cache, int32_t layer, const uin
  * in fp64, then encoded as in kv_store_fp8.  A pair holding a NaN code
  * becomes 0x7F in both places.  Dims >= rot_dim are not touched.
  *
- * slots (device): int64 [n_slots] cache slots to shift (< 0 skipped; no
- *   repeats).  rot_dim even, 2 <= rot_dim <= head_dim.  theta_base finite
+ * slots (device): int64 [n_slots] cache slots to shift (< 0 and >=
+ *   num_blocks * block_size skipped; no repeats).  rot_dim even, 2 <= rot_dim <= head_dim.  theta_base finite
  *   and > 0.
  */
 kvf8_status kv_shift_rope(kvf8_cache *cache, int32_t layer, const int64_t *slots,

@@ -68,7 +68,7 @@ def _load():
         "orc_k_tile_offset": (i64, [ctypes.c_int] * 4),
         "orc_v_tile_offset": (i64, [ctypes.c_int] * 4),
         "orc_store": (None, [P, P, i64, i64, P, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                             f32, f32, P, P]),
+                             i64, f32, f32, P, P]),
         "orc_gather_dequant": (None, [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P,
                                       ctypes.c_int, ctypes.c_int, f32, f32, P, P]),
         "orc_decode_attn": (ctypes.c_int, [P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int,
@@ -78,7 +78,7 @@ def _load():
                                             ctypes.c_int, P, P, P, ctypes.c_int, ctypes.c_int,
                                             f32, f32, f64, P, i64, P]),
         "orc_rope_table": (None, [ctypes.c_int, ctypes.c_int, f32, P, P]),
-        "orc_kshift": (ctypes.c_int, [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, i64,
+        "orc_kshift": (ctypes.c_int, [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, P, i64,
                                       ctypes.c_int, f32, ctypes.c_int, ctypes.c_int]),
         "orc_kv_bytes_per_block": (i64, [ctypes.c_int] * 4),
     }
@@ -146,17 +146,17 @@ def store(k_bits, v_bits, slots, k_pool, v_pool, *, Hkv: int, D: int, BS: int,
           k_scale: float, v_scale: float) -> None:
     """Quantize bf16 K/V rows [T][Hkv][D] into the byte pools in place.
 
-    k_pool / v_pool: uint8 arrays [NB][Hkv][BS*D] (modified in place)."""
+    k_pool / v_pool: uint8 arrays [NB][Hkv][BS*D] (modified in place).  Slots
+    that are negative or at or past NB*BS are skipped."""
     k = _c(k_bits, np.uint16).reshape(-1, Hkv * D)
     v = _c(v_bits, np.uint16).reshape(-1, Hkv * D)
     s = _c(slots, np.int64)
     assert k.shape[0] == v.shape[0] == s.shape[0]
     assert k_pool.dtype == np.uint8 and v_pool.dtype == np.uint8
     assert k_pool.flags.c_contiguous and v_pool.flags.c_contiguous
-    nb_tokens = k_pool.size // (Hkv * D)
-    if s.size and s.max() >= nb_tokens:
-        raise ValueError("slot out of range")
-    _load().orc_store(_ptr(k), _ptr(v), Hkv * D, Hkv * D, _ptr(s), s.size, Hkv, D, BS,
+    assert k_pool.size == v_pool.size and k_pool.size % (Hkv * BS * D) == 0
+    NB = k_pool.size // (Hkv * BS * D)
+    _load().orc_store(_ptr(k), _ptr(v), Hkv * D, Hkv * D, _ptr(s), s.size, Hkv, D, BS, NB,
                       float(np.float32(k_scale)), float(np.float32(v_scale)),
                       _ptr(k_pool), _ptr(v_pool))
 
@@ -232,10 +232,13 @@ def rope_table(rot_dim: int, delta: int, theta: float):
 
 def kshift(k_pool, slots, *, Hkv: int, D: int, BS: int, delta: int, theta: float, rot_dim: int,
            neox: bool) -> None:
-    """Re-rotate cached K by a RoPE position delta, in place (scale-free)."""
+    """Re-rotate cached K by a RoPE position delta, in place (scale-free).  Slots
+    that are negative or at or past the pool's NB*BS slots are skipped."""
     s = _c(slots, np.int64)
     assert k_pool.dtype == np.uint8 and k_pool.flags.c_contiguous
-    rc = _load().orc_kshift(_ptr(k_pool), Hkv, D, BS, _ptr(s), s.size, int(delta),
+    assert k_pool.size % (Hkv * BS * D) == 0
+    NB = k_pool.size // (Hkv * BS * D)
+    rc = _load().orc_kshift(_ptr(k_pool), Hkv, D, BS, NB, _ptr(s), s.size, int(delta),
                             float(np.float32(theta)), rot_dim, 1 if neox else 0)
     if rc != 0:
         raise MemoryError("oracle scratch allocation failed")

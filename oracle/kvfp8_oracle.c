@@ -175,20 +175,21 @@ static int64_t orc_tile_base(int64_t block, int h, int Hkv, int BS, int D)
 /* V/s_v; P2, quantize_row_f8_e4m3_ref].  x is the bf16 input widened   */
 /* to fp32, y = fl32(x * fl32(1/s)), code = encode(y).  IEEE 754 leaves */
 /* the sign of a NaN produced by a multiply unspecified, so a NaN input */
-/* keeps its own sign.  A negative slot means "skip this token".        */
+/* keeps its own sign.  A negative slot, or one at or past the pool's   */
+/* NB * BS slots, means "skip this token".                              */
 /* k, v: [T][Hkv][D] bf16 bits with a token stride in elements.         */
 /* ------------------------------------------------------------------ */
 void orc_store(const uint16_t *k, const uint16_t *v,
                int64_t k_tok_stride, int64_t v_tok_stride,
                const int64_t *slots, int64_t T,
-               int Hkv, int D, int BS, float k_scale, float v_scale,
+               int Hkv, int D, int BS, int64_t NB, float k_scale, float v_scale,
                uint8_t *k_pool, uint8_t *v_pool)
 {
     const float k_inv = 1.0f / k_scale;
     const float v_inv = 1.0f / v_scale;
     for (int64_t i = 0; i < T; ++i) {
         const int64_t slot = slots[i];
-        if (slot < 0)
+        if (slot < 0 || slot >= NB * BS)
             continue;
         const int64_t block = slot / BS;
         const int t = (int)(slot % BS);
@@ -372,6 +373,7 @@ int orc_prefill_attn(const uint16_t *q, int Hq,
 /* values and rounded to fp32 before encoding.  A pair holding a NaN    */
 /* code becomes the NaN code 0x7F in both places (the sign of an        */
 /* arithmetic NaN is not defined by IEEE 754).  Dims >= rot untouched.  */
+/* Slots < 0 or at or past the pool's NB * BS slots are skipped.        */
 /* ------------------------------------------------------------------ */
 void orc_rope_table(int rot_dim, int delta, float theta, float *cos_out, float *sin_out)
 {
@@ -383,7 +385,7 @@ void orc_rope_table(int rot_dim, int delta, float theta, float *cos_out, float *
     }
 }
 
-int orc_kshift(uint8_t *k_pool, int Hkv, int D, int BS,
+int orc_kshift(uint8_t *k_pool, int Hkv, int D, int BS, int64_t NB,
                const int64_t *slots, int64_t n_slots,
                int delta, float theta, int rot_dim, int style)
 {
@@ -396,7 +398,7 @@ int orc_kshift(uint8_t *k_pool, int Hkv, int D, int BS,
     orc_rope_table(rot_dim, delta, theta, cs, sn);
     for (int64_t i = 0; i < n_slots; ++i) {
         const int64_t slot = slots[i];
-        if (slot < 0)
+        if (slot < 0 || slot >= NB * BS)
             continue;
         const int64_t block = slot / BS;
         const int t = (int)(slot % BS);

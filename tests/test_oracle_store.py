@@ -197,3 +197,20 @@ def test_fp8_block_bytes_are_exactly_half(orc, BS, Hkv, D):
     assert fp8 == 2 * BS * Hkv * D      # K and V, one byte per element
     budget = 1 << 30
     assert budget // fp8 >= 2 * (budget // bf16)   # a byte budget at least doubles the block count
+
+
+def test_slots_past_the_pool_are_skipped(orc):
+    """Negative slots and slots at or past NB*BS are skipped by the store and the
+    K-shift (the boundary's contract): nothing is written, nothing outside the pool."""
+    Hkv, D, BS, NB = 2, 64, 16, 3
+    kp = np.zeros((NB, Hkv, BS * D), np.uint8)
+    vp = np.zeros_like(kp)
+    x = bf16_bits(torch.ones((4, Hkv, D), dtype=torch.bfloat16))
+    orc.store(x, x, np.array([NB * BS, NB * BS + 5, -3, 1 << 40]), kp, vp, Hkv=Hkv, D=D, BS=BS,
+              k_scale=1.0, v_scale=1.0)
+    assert not kp.any() and not vp.any()
+    kp[:] = 0x38
+    before = kp.copy()
+    orc.kshift(kp, np.array([NB * BS, -1, 1 << 40]), Hkv=Hkv, D=D, BS=BS, delta=3, theta=1e4,
+               rot_dim=D, neox=True)
+    assert np.array_equal(kp, before)
