@@ -414,8 +414,8 @@ kvf8_status paged_attn_prefill_chunk(kvf8_cache *c, int32_t layer, const uint16_
         return fail(KVF8_E_INVALID, "sm_scale must be finite and > 0");
     if (out_dtype != KVF8_DTYPE_F32 && out_dtype != KVF8_DTYPE_BF16)
         return fail(KVF8_E_INVALID, "out_dtype must be KVF8_DTYPE_F32 or KVF8_DTYPE_BF16");
-    if ((int64_t)max_ctx_len + max_q_len > (int64_t)max_blocks_per_seq * c->block_size)
-        return fail(KVF8_E_INVALID, "max_ctx_len + max_q_len exceeds max_blocks_per_seq * block_size");
+    if ((int64_t)max_q_len > (int64_t)max_blocks_per_seq * c->block_size)
+        return fail(KVF8_E_INVALID, "max_q_len exceeds max_blocks_per_seq * block_size");
     if (num_seqs == 0 || total_q == 0) return ok();
     if (!q_bf16 || !cu_q_lens || !context_lens || !block_tables || !out)
         return fail(KVF8_E_INVALID, "q, cu_q_lens, context_lens, block_tables and out must be non-NULL");

@@ -226,8 +226,10 @@ kvf8_status paged_attn_decode(kvf8_cache *cache, int32_t layer, const uint16_t *
  *   back to back.  cu_q_lens (device): int32 [num_seqs+1], cu_q_lens[0] = 0,
  *   non-decreasing, cu_q_lens[num_seqs] = total_q.  context_lens (device):
  *   int32 [num_seqs].  block_tables (device): as in paged_attn_decode,
- *   covering context + chunk.  max_q_len / max_ctx_len (host): upper bounds
- *   of the chunk lengths and context lengths, size the launch.
+ *   covering context + chunk: context_lens[b] + q_len_b must not exceed
+ *   max_blocks_per_seq * block_size (keys past the table row are never
+ *   read).  max_q_len / max_ctx_len (host): upper bounds of the chunk lengths
+ *   and context lengths, size the launch.
  * out (device): [total_q][num_q_heads][head_dim], fp32 or bf16.
  */
 kvf8_status paged_attn_prefill_chunk(kvf8_cache *cache, int32_t layer, const uint16_t *q_bf16,
