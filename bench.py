@@ -39,7 +39,9 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama8b", choices=["llama8b"])
+    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "prefill", "longctx", "varlen"])
+    ap.add_argument("--pool-frac", type=float, default=0.5,
+                    help="varlen: fraction of 288 GB used for the block pool")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the CPU-oracle sample time (0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -221,9 +223,10 @@ def run_llama8b(args):
 
 
 def _cpu_baseline(w, K, V, slots, q, out, ks, vs, budget_s):
-    """The CPU oracle on a bounded sample: whole (sequence, kv-head) groups, all
-    query heads of each group, until the time budget is used.  Also compares the
-    GPU decode output on those heads with the oracle (the same formula as the tests)."""
+    """The CPU oracle on a bounded sample: (sequence, kv-head) groups in a seeded
+    order, all query heads of each group, until the time budget is used.  Also
+    compares the GPU decode output on those heads with the oracle (the same
+    tolerance as the tests)."""
     import oracle
     from synth import bf16_bits
     q_bits = bf16_bits(q)
@@ -231,17 +234,19 @@ def _cpu_baseline(w, K, V, slots, q, out, ks, vs, budget_s):
     G = w.Hq // w.Hkv
     row = w.Hkv * w.D
     rng = np.random.default_rng(7)
-    order = [(int(b), int(h)) for b, h in zip(rng.permutation(w.B), rng.integers(0, w.Hkv, w.B))]
+    order = [(int(i // w.Hkv), int(i % w.Hkv)) for i in rng.permutation(w.B * w.Hkv)]
     kp = np.zeros((w.NB, w.Hkv, w.BS * w.D), np.uint8)
     vp = np.zeros_like(kp)
     offs = np.concatenate([[0], np.cumsum(w.total_lengths)])
-    done, elapsed, worst = 0, 0.0, 0.0
-    bad = 0
+    stored = set()
+    done, elapsed, worst, bad, nbytes = 0, 0.0, 0.0, 0, 0
     for b, kvh in order:
         lo, hi = int(offs[b]), int(offs[b + 1])
-        kb = bf16_bits(K[lo:hi]).reshape(hi - lo, row)
-        vb = bf16_bits(V[lo:hi]).reshape(hi - lo, row)
-        oracle.store(kb, vb, slots[lo:hi], kp, vp, Hkv=w.Hkv, D=w.D, BS=w.BS, k_scale=ks, v_scale=vs)
+        if b not in stored:
+            kb = bf16_bits(K[lo:hi]).reshape(hi - lo, row)
+            vb = bf16_bits(V[lo:hi]).reshape(hi - lo, row)
+            oracle.store(kb, vb, slots[lo:hi], kp, vp, Hkv=w.Hkv, D=w.D, BS=w.BS, k_scale=ks, v_scale=vs)
+            stored.add(b)
         sel = np.array([[b, kvh * G + j] for j in range(G)], np.int32)
         t0 = time.perf_counter()
         ref = oracle.decode_attn(q_bits, kp, vp, w.block_tables, w.total_lengths.astype(np.int32),
@@ -252,18 +257,277 @@ def _cpu_baseline(w, K, V, slots, q, out, ks, vs, budget_s):
             err = np.abs(got[b, hh] - ref[b, hh])
             worst = max(worst, float(err.max()))
             bad += int((err > 2e-3 + 1e-2 * np.abs(ref[b, hh])).sum())
+        L = int(w.total_lengths[b])
+        nbytes += L * 2 * w.D + G * w.D * (2 + 2) + 4 * (-(-L // w.BS)) + 4
         done += 1
         if elapsed >= budget_s:
             break
-    L = int(w.total_lengths[0])
-    sample_bytes = done * (L * 2 * w.D + G * w.D * (2 + 2) + 4 * (-(-L // w.BS)) + 4)
-    cpu = {"value": round(sample_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
-           "kind": "oracle",
-           "sample": f"{done} (sequence, kv-head) groups x {G} query heads x {L} tokens, fp64 "
+    cpu = {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{done} of {w.B * w.Hkv} (sequence, kv-head) groups x {G} query heads, fp64 "
                      f"single-threaded C oracle, {elapsed:.1f} s",
            "tokens_per_s": round(done * G / w.Hq / elapsed, 4)}
     parity = {"heads_checked": done * G, "max_abs_err_bf16_out": worst, "outside_tolerance": bad}
     return cpu, parity
+
+
+def _fill(w, kv, dev, stream, copies=1, upto=None, empty=False):
+    """Store tokens 0..upto[b]-1 of every sequence into `copies` caches (untimed setup).
+    Returns (pools, handles)."""
+    import torch
+    ks, vs, _ = w.scales()
+    row = w.Hkv * w.D
+    pools, handles = [], []
+    for _ in range(copies):
+        alloc = torch.empty if empty else torch.zeros
+        kp = alloc((w.NB, w.Hkv, w.BS * w.D), dtype=torch.uint8, device=dev)
+        vp = alloc((w.NB, w.Hkv, w.BS * w.D), dtype=torch.uint8, device=dev)
+        handles.append(kv.kv_cache_alloc(1, w.NB, w.BS, w.Hkv, w.D, [float(ks)], [float(vs)],
+                                         kv.DTYPE_F32, kp, vp))
+        pools.append((kp, vp))
+    upto = w.lengths if upto is None else upto
+    step = 65536
+    for b in range(w.B):
+        L = int(upto[b])
+        for lo in range(0, L, step):
+            n = min(step, L - lo)
+            k, v = w.kv(b, lo, n, device=dev)
+            sd = torch.from_numpy(w.slots(b, lo, n)).to(dev)
+            for h in handles:
+                kv.kv_store_fp8(h, 0, k.reshape(n, row), v.reshape(n, row), row, row, sd, n, stream)
+    torch.cuda.synchronize()
+    return pools, handles
+
+
+def _timed(fn, steps, warmup, stream):
+    """Per-launch HIP-event times (ms) of fn(i), back to back on `stream`."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    ev = []
+    for i in range(steps):
+        _time_ms(lambda: fn(i), stream, ev)
+    torch.cuda.synchronize()
+    return np.array([s.elapsed_time(e) for s, e in ev])
+
+
+def _stats(ms):
+    return {"ms_mean": round(float(ms.mean()), 5), "ms_p10": round(float(np.percentile(ms, 10)), 5),
+            "ms_p50": round(float(np.percentile(ms, 50)), 5), "ms_p90": round(float(np.percentile(ms, 90)), 5)}
+
+
+def _decode_bytes(w, lens, out_bytes):
+    blocks = int(sum(-(-int(L) // w.BS) for L in lens))
+    return int(np.sum(lens)) * 2 * w.Hkv * w.D + w.B * w.Hq * w.D * (2 + out_bytes) + 4 * blocks + 4 * w.B
+
+
+def _header(args, workload, value, unit, ms_per_step, config):
+    return {"metric": "fp8-KV paged decode attn achieved HBM GB/s + tokens/s; kv_store tokens/s",
+            "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp8_e4m3 cache; bf16/f16 MFMA, f32 accumulate",
+            "data": "synthetic", "config": dict(workload=workload, **config)}
+
+
+def run_prefill(args):
+    """Chunked prefill: 4 sequences x (16384 cached + 2048 new) tokens, 32 q / 8 kv heads,
+    head_dim 128, block 16.  Step = kv_store_fp8 of the 8192 chunk tokens + the causal
+    prefill of their queries.  Roofline: the prefill kernel against the bf16/f16 MFMA peak."""
+    import torch
+    import fp8_e4m3_scaled_amd as kv
+    from synth import Workload
+    dev, stream = torch.device("cuda:0"), torch.cuda.current_stream()
+    w = Workload("prefill", device=dev)
+    pools, handles = _fill(w, kv, dev, stream)
+    h = handles[0]
+    n = w.spec.new_tokens
+    row = w.Hkv * w.D
+    ctx = w.lengths.astype(np.int32)
+    K = torch.cat([w.kv(b, int(ctx[b]), n, device=dev)[0].reshape(n, row) for b in range(w.B)])
+    V = torch.cat([w.kv(b, int(ctx[b]), n, device=dev)[1].reshape(n, row) for b in range(w.B)])
+    sd = torch.from_numpy(np.concatenate([w.slots(b, int(ctx[b]), n) for b in range(w.B)])).to(dev)
+    T = w.B * n
+    q = w.q_chunk(dev)
+    cu = torch.from_numpy((np.arange(w.B + 1) * n).astype(np.int32)).to(dev)
+    ctx_d = torch.from_numpy(ctx).to(dev)
+    tables = torch.from_numpy(w.block_tables.astype(np.int32)).to(dev)
+    out = torch.empty((T, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+
+    def store(i):
+        kv.kv_store_fp8(h, 0, K, V, row, row, sd, T, stream)
+
+    def prefill(i):
+        kv.paged_attn_prefill_chunk(h, 0, q, w.Hq, cu, ctx_d, tables, w.max_blocks, w.B, T, n,
+                                    int(ctx.max()), w.sm_scale(), out, kv.DTYPE_BF16, stream)
+
+    st = _timed(store, args.steps, args.warmup, stream)
+    pf = _timed(prefill, args.steps, args.warmup, stream)
+    flops = sum(4 * w.D * w.Hq * (int(ctx[b]) * n + n * (n + 1) // 2) for b in range(w.B))
+    tflops = flops / (pf.mean() * 1e-3) / 1e12
+    store_bytes = T * (6 * w.Hkv * w.D + 8)
+    res = _header(args, "prefill", round(tflops, 1), "TFLOP/s", float(st.mean() + pf.mean()),
+                  {"q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D, "block_size": w.BS,
+                   "num_seqs": w.B, "context": int(ctx[0]), "chunk": n, "out_dtype": "bf16"})
+    res["prefill"] = dict(_stats(pf), flops=flops, tflops=round(tflops, 2),
+                          frac_mfma_peak=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                          tokens_per_s=round(T / (pf.mean() * 1e-3), 1))
+    res["kv_store"] = dict(_stats(st), tokens=T, algorithmic_bytes=store_bytes,
+                           tokens_per_s=round(T / (st.mean() * 1e-3), 1),
+                           GBps=round(store_bytes / (st.mean() * 1e-3) / 1e9, 1))
+    res["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "traffic": None, "kernel": "prefill_kernel<128,16>"}
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = _cpu_prefill(w, q, out, ctx, n, args.cpu_seconds)
+    kv.kv_cache_free(h)
+    return res
+
+
+def _cpu_prefill(w, q, out, ctx, n, budget_s):
+    """Oracle FLOP/s on sampled query rows (and their parity with the GPU output)."""
+    import oracle
+    from synth import bf16_bits
+    # the oracle reads bytes that it stored itself: store every sequence again on the CPU
+    okp = np.zeros((w.NB, w.Hkv, w.BS * w.D), np.uint8)
+    ovp = np.zeros_like(okp)
+    row = w.Hkv * w.D
+    for b in range(w.B):
+        L = int(w.total_lengths[b])
+        for lo in range(0, L, 8192):
+            m = min(8192, L - lo)
+            k, v = w.kv(b, lo, m, device=q.device)
+            oracle.store(bf16_bits(k).reshape(m, row), bf16_bits(v).reshape(m, row), w.slots(b, lo, m),
+                         okp, ovp, Hkv=w.Hkv, D=w.D, BS=w.BS, k_scale=w.scales()[0], v_scale=w.scales()[1])
+    qb = bf16_bits(q)
+    got = out.float().cpu().numpy()
+    cu = (np.arange(w.B + 1) * n).astype(np.int32)
+    rng = np.random.default_rng(11)
+    done, flops, elapsed, bad = 0, 0, 0.0, 0
+    ks, vs, _ = w.scales()
+    while elapsed < budget_s and done < 4096:
+        r = int(rng.integers(0, w.B * n))
+        hh = int(rng.integers(0, w.Hq))
+        t0 = time.perf_counter()
+        ref = oracle.prefill_attn(qb, okp, ovp, cu, ctx, w.block_tables, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
+                                  BS=w.BS, k_scale=ks, v_scale=vs, sm_scale=w.sm_scale(),
+                                  sel=np.array([[r, hh]], np.int64))
+        elapsed += time.perf_counter() - t0
+        b = r // n
+        keys = int(ctx[b]) + (r - b * n) + 1
+        flops += 4 * w.D * keys
+        err = np.abs(got[r, hh] - ref[r, hh])
+        bad += int((err > 2e-3 + 1e-2 * np.abs(ref[r, hh])).sum())
+        done += 1
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} random (query row, head) pairs, fp64 single-threaded C oracle "
+                      f"(including the per-row dequantizing gather), {elapsed:.1f} s",
+            "parity_outside_tolerance": bad}
+
+
+def run_longctx(args):
+    """Long context + K-shift: 8 sequences x 131072 tokens, 16 q / 2 kv heads, head_dim 256,
+    block 32, scales 0.03.  Step = decode, kv_shift_rope of every cached token by -4096
+    (theta 1e6, NEOX), decode.  Roofline: the decode kernel against HBM."""
+    import torch
+    import fp8_e4m3_scaled_amd as kv
+    from synth import Workload
+    dev, stream = torch.device("cuda:0"), torch.cuda.current_stream()
+    w = Workload("longctx", device=dev)
+    copies = 3
+    pools, handles = _fill(w, kv, dev, stream, copies=copies)
+    lens = w.lengths.astype(np.int32)
+    max_len = int(lens.max())
+    q = w.q_decode(dev)
+    tables = torch.from_numpy(w.block_tables.astype(np.int32)).to(dev)
+    lens_d = torch.from_numpy(lens).to(dev)
+    slots = torch.from_numpy(np.concatenate([w.slots(b, 0, int(lens[b])) for b in range(w.B)])).to(dev)
+    nsl = int(slots.numel())
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+    ws_bytes = kv.paged_attn_decode_workspace(handles[0], w.B, w.Hq, max_len)
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
+
+    def decode(i):
+        kv.paged_attn_decode(handles[i % copies], 0, q, w.Hq, tables, w.max_blocks, lens_d, w.B, max_len,
+                             w.sm_scale(), out, kv.DTYPE_BF16, ws, ws_bytes, stream)
+
+    def shift(i):
+        kv.kv_shift_rope(handles[i % copies], 0, slots, nsl, w.spec.delta, w.spec.theta, w.D,
+                         kv.ROPE_NEOX, stream)
+
+    de = _timed(decode, args.steps, args.warmup, stream)
+    sh = _timed(shift, args.steps, args.warmup, stream)
+    de_bytes = _decode_bytes(w, lens, 2)
+    sh_bytes = nsl * (2 * w.Hkv * w.D + 8)
+    de_gbps = de_bytes / (de.mean() * 1e-3) / 1e9
+    sh_gbps = sh_bytes / (sh.mean() * 1e-3) / 1e9
+    res = _header(args, "longctx", round(de_gbps, 1), "GB/s", float(2 * de.mean() + sh.mean()),
+                  {"q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D, "block_size": w.BS,
+                   "num_seqs": w.B, "seq_len": max_len, "shift_delta": w.spec.delta,
+                   "rope_theta": w.spec.theta, "out_dtype": "bf16", "decode_splits": ws_bytes > 0})
+    res["decode"] = dict(_stats(de), algorithmic_bytes=de_bytes, GBps=round(de_gbps, 1),
+                         frac_hbm_peak=round(de_gbps / HBM_PEAK_GBPS, 4),
+                         tokens_per_s=round(w.B / (de.mean() * 1e-3), 1))
+    res["kv_shift"] = dict(_stats(sh), algorithmic_bytes=sh_bytes, GBps=round(sh_gbps, 1),
+                           frac_hbm_peak=round(sh_gbps / HBM_PEAK_GBPS, 4),
+                           tokens_per_s=round(nsl / (sh.mean() * 1e-3), 1))
+    res["roofline"] = {"bound": "hbm", "achieved": round(de_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                       "frac": round(de_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                       "kernel": "decode_kernel<256,32> + decode_reduce<256>"}
+    for h in handles:
+        kv.kv_cache_free(h)
+    return res
+
+
+def run_varlen(args):
+    """Variable-length decode: 256 sequences with lengths uniform in [512, 32768], 32 q / 8 kv
+    heads, head_dim 128, block 16, bf16 scales, block tables drawn from a shuffled free list
+    over a pool that is --pool-frac of 288 GB.  Step = kv_store_fp8 of one new token per
+    sequence (at position L) + decode over L+1 tokens.  Roofline: the decode kernel."""
+    import torch
+    import fp8_e4m3_scaled_amd as kv
+    from synth import Workload
+    dev, stream = torch.device("cuda:0"), torch.cuda.current_stream()
+    w = Workload("varlen", device=dev, pool_frac=args.pool_frac)
+    pools, handles = _fill(w, kv, dev, stream, empty=True)
+    h = handles[0]
+    row = w.Hkv * w.D
+    L = w.lengths
+    K = torch.cat([w.kv(b, int(L[b]), 1, device=dev)[0].reshape(1, row) for b in range(w.B)])
+    V = torch.cat([w.kv(b, int(L[b]), 1, device=dev)[1].reshape(1, row) for b in range(w.B)])
+    sd = torch.from_numpy(np.concatenate([w.slots(b, int(L[b]), 1) for b in range(w.B)])).to(dev)
+    lens = w.total_lengths.astype(np.int32)
+    max_len = int(lens.max())
+    q = w.q_decode(dev)
+    tables = torch.from_numpy(w.block_tables.astype(np.int32)).to(dev)
+    lens_d = torch.from_numpy(lens).to(dev)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+    ws_bytes = kv.paged_attn_decode_workspace(h, w.B, w.Hq, max_len)
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
+
+    def store(i):
+        kv.kv_store_fp8(h, 0, K, V, row, row, sd, w.B, stream)
+
+    def decode(i):
+        kv.paged_attn_decode(h, 0, q, w.Hq, tables, w.max_blocks, lens_d, w.B, max_len, w.sm_scale(),
+                             out, kv.DTYPE_BF16, ws, ws_bytes, stream)
+
+    st = _timed(store, args.steps, args.warmup, stream)
+    de = _timed(decode, args.steps, args.warmup, stream)
+    de_bytes = _decode_bytes(w, lens, 2)
+    de_gbps = de_bytes / (de.mean() * 1e-3) / 1e9
+    res = _header(args, "varlen", round(de_gbps, 1), "GB/s", float(st.mean() + de.mean()),
+                  {"q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D, "block_size": w.BS,
+                   "num_seqs": w.B, "max_seq_len": max_len, "mean_seq_len": float(lens.mean()),
+                   "pool_blocks": int(w.NB), "pool_frac_of_288GB": args.pool_frac, "scale_dtype": "bf16",
+                   "out_dtype": "bf16"})
+    res["decode"] = dict(_stats(de), algorithmic_bytes=de_bytes, GBps=round(de_gbps, 1),
+                         frac_hbm_peak=round(de_gbps / HBM_PEAK_GBPS, 4),
+                         tokens_per_s=round(w.B / (de.mean() * 1e-3), 1))
+    res["kv_store"] = dict(_stats(st), tokens=w.B, tokens_per_s=round(w.B / (st.mean() * 1e-3), 1))
+    res["roofline"] = {"bound": "hbm", "achieved": round(de_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                       "frac": round(de_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                       "kernel": "decode_kernel<128,16> + decode_reduce<128>"}
+    kv.kv_cache_free(h)
+    return res
 
 
 def main():
@@ -276,8 +540,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    res = run_llama8b(args)
-    print(json.dumps(res), flush=True)
+    run = {"llama8b": run_llama8b, "prefill": run_prefill, "longctx": run_longctx,
+           "varlen": run_varlen}[args.workload]
+    print(json.dumps(run(args)), flush=True)
 
 
 if __name__ == "__main__":
