@@ -55,6 +55,14 @@ class KvF8Error(RuntimeError):
 def _load_library():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m fp8_e4m3_scaled_amd.build`")
+    # torch ships its own HIP runtime under the same soname as the system one.
+    # Loading torch first makes the library bind to that copy, so the process
+    # holds one HIP runtime; a second runtime would find the device already
+    # claimed by the first and report that no device exists.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

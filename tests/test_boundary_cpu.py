@@ -207,3 +207,23 @@ def test_workspace_size_is_consistent():
             assert n >= 0 and n % 4 == 0
     finally:
         kv.kv_cache_free(c)
+
+
+@pytest.mark.parametrize("order", ["package_first", "torch_first"])
+def test_one_hip_runtime_per_process(order):
+    """Whatever the import order, the library and torch share one HIP runtime:
+    two runtimes in one process make the second one see no device."""
+    import subprocess
+    import sys
+    mods = ["fp8_e4m3_scaled_amd", "torch"]
+    if order == "torch_first":
+        mods.reverse()
+    code = (
+        "import importlib, sys\n"
+        f"sys.path.insert(0, {os.path.dirname(os.path.dirname(os.path.abspath(__file__)))!r})\n"
+        f"for m in {mods!r}: importlib.import_module(m)\n"
+        "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+        "print(len(maps), sorted(maps))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.startswith("1 "), out.stdout
