@@ -37,6 +37,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+static_assert(kThreads == kDecodeThreads, "host launch checks assume this workgroup size");
 constexpr int kStep = 32;                 // tokens per wave step
 constexpr float kLazy = 8.0f;             // log2 headroom of the lazy softmax reference
 
@@ -207,6 +208,23 @@ __device__ __forceinline__ void compute_step(SoftmaxState<D> &st, StepRegs<D> &c
 template <int D>
 struct Depth { static constexpr int NBUF = D >= 256 ? 2 : 3; };
 
+// Workgroups are handed to the 8 XCDs round-robin by linear id, and each XCD
+// has its own CUs and L2.  Unit (pair p = seq * kv_heads + kv_head, split s)
+// runs as linear id h with h % 8 == (p + s) % 8: the splits of one pair rotate
+// over the XCDs and neighbouring pairs interleave, so every XCD receives an
+// even share of the work whatever the sequence lengths and the split count
+// (with the plain (split, head, seq) grid and 8 splits, every first chunk
+// landed on one XCD).  Ids run split-major; pairs are padded to a multiple of
+// 8 and padding units exit at once.
+__device__ __forceinline__ bool decode_unit(uint32_t h, const DecodeArgs &a, int &pair, int &split) {
+    const int pairs = a.num_seqs * a.kv_heads;
+    const uint32_t per = (uint32_t)((pairs + 7) >> 3);
+    const uint32_t k = h >> 3;
+    split = (int)(k / per);
+    pair = (((int)(h & 7) - split) & 7) + 8 * (int)(k % per);
+    return pair < pairs;
+}
+
 template <int D, int BS>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     constexpr int KK = D / 32;     // QK^T instructions per tile
@@ -215,9 +233,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
     extern __shared__ float smem[];   // [waves][G] max, [waves][G] sum, [waves][G][D] acc
 
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z;
+    int pair, split;
+    if (!decode_unit(blockIdx.x, a, pair, split)) return;   // padding unit
+    const int kvh = pair % a.kv_heads;
+    const int b = pair / a.kv_heads;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int m = lane & 15;        // MFMA row/column index of this lane
@@ -286,10 +305,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         load_step<D, BS>(r, a.k_pool, a.v_pool, b0, b1, a.kv_heads, kvh, p0 + ii * stride, m, g, live);
     };
     StepRegs<D> buf[NBUF];
-    if (nsteps > 0) {
+    // Unconditional, so that every path into the loop holds the same loads in
+    // flight (a wave with no steps issues dummy loads of one valid line).
 #pragma unroll
-        for (int i = 0; i < NBUF - 1; ++i) issue(buf[i], i);
-    }
+    for (int i = 0; i < NBUF - 1; ++i) issue(buf[i], i);
     for (int i = 0; i < nsteps; i += NBUF) {
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
@@ -356,34 +375,70 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 }
 
 // Combine split partials: o = v_scale * sum_i acc_i 2^(m_i - M) / sum_i l_i 2^(m_i - M).
+// The split maxima and weights are computed one split per thread and staged in
+// LDS; each output dim then sums its partials with independent loads.
 template <int D>
 __global__ __launch_bounds__(D) void decode_reduce(DecodeArgs a) {
+    constexpr int kBatch = D;            // splits weighted per pass
+    __shared__ float s_w[kBatch];
+    __shared__ float s_red[D / 64];
     const int head = blockIdx.x;
     const int b = blockIdx.y;
-    const int d = threadIdx.x;
+    const int t = threadIdx.x;
     const int L = a.seq_lens[b];   // clamped the same way as in decode_kernel
     const int Lc = min(L, a.max_blocks * a.block_size);
     const int nsplit = Lc <= 0 ? 0 : min(a.splits, (Lc + a.chunk_tokens - 1) / a.chunk_tokens);
     const float *part = a.partials + ((int64_t)b * a.q_heads + head) * a.splits * (D + 2);
-    float M = -__builtin_inff();
-    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, part[i * (D + 2)]);
+
+    float m = -__builtin_inff();
+    for (int i = t; i < nsplit; i += D) m = fmaxf(m, part[(int64_t)i * (D + 2)]);
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((t & 63) == 0) s_red[t >> 6] = m;
+    __syncthreads();
+    float M = s_red[0];
+#pragma unroll
+    for (int w = 1; w < D / 64; ++w) M = fmaxf(M, s_red[w]);
+
     float num = 0.0f, den = 0.0f;
-    for (int i = 0; i < nsplit; ++i) {
-        const float mi = part[i * (D + 2)];
-        const float f = mi == -__builtin_inff() ? 0.0f : exp2f(mi - M);
-        num += f * part[i * (D + 2) + 2 + d];
-        den += f * part[i * (D + 2) + 1];
+    for (int i0 = 0; i0 < nsplit; i0 += kBatch) {
+        const int n = min(kBatch, nsplit - i0);
+        __syncthreads();                 // s_red / previous batch consumed
+        if (t < n) {
+            const float *p = part + (int64_t)(i0 + t) * (D + 2);
+            const float mi = p[0];
+            s_w[t] = mi == -__builtin_inff() ? 0.0f : exp2f(mi - M);
+        }
+        __syncthreads();
+        const float *p = part + (int64_t)i0 * (D + 2);
+        int i = 0;
+        for (; i + 8 <= n; i += 8) {
+            float x[8], l[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                x[u] = p[(int64_t)(i + u) * (D + 2) + 2 + t];
+                l[u] = p[(int64_t)(i + u) * (D + 2) + 1];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                num += s_w[i + u] * x[u];
+                den += s_w[i + u] * l[u];
+            }
+        }
+        for (; i < n; ++i) {
+            num += s_w[i] * p[(int64_t)i * (D + 2) + 2 + t];
+            den += s_w[i] * p[(int64_t)i * (D + 2) + 1];
+        }
     }
     const float o = nsplit > 0 ? num * a.v_scale / den : 0.0f;
-    store_out(a.out, ((int64_t)b * a.q_heads + head) * D + d, o, a.out_bf16);
+    store_out(a.out, ((int64_t)b * a.q_heads + head) * D + t, o, a.out_bf16);
 }
 
 template <int D, int BS>
 hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     const int G = a.q_heads / a.kv_heads;
     const size_t smem = sizeof(float) * (size_t)kWaves * G * (2 + D);
-    hipLaunchKernelGGL((decode_kernel<D, BS>), dim3(a.splits, a.kv_heads, a.num_seqs), dim3(kThreads), smem,
-                       stream, a);
+    const uint32_t units = (uint32_t)a.splits * (uint32_t)(((a.num_seqs * a.kv_heads + 7) >> 3) << 3);
+    hipLaunchKernelGGL((decode_kernel<D, BS>), dim3(units), dim3(kThreads), smem, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     hipLaunchKernelGGL((decode_reduce<D>), dim3(a.q_heads, a.num_seqs), dim3(D), 0, stream, a);

@@ -367,6 +367,10 @@ kvf8_status paged_attn_decode(kvf8_cache *c, int32_t layer, const uint16_t *q_bf
         return fail(KVF8_E_INVALID, "q must be 16-byte aligned");
     int32_t splits = 1, chunk = 0;
     kvf8::decode_plan(num_seqs, c->kv_heads, c->head_dim, c->block_size, max_seq_len, &splits, &chunk);
+    // one workgroup per (sequence, kv head, split), pairs padded to a multiple of 8
+    const int64_t units = (int64_t)splits * ((((int64_t)num_seqs * c->kv_heads) + 7) / 8 * 8);
+    if (units * kvf8::kDecodeThreads >= ((int64_t)1 << 32))
+        return fail(KVF8_E_UNSUPPORTED, "%lld decode workgroups exceed one launch", (long long)units);
     const size_t need = paged_attn_decode_workspace(c, num_seqs, num_q_heads, max_seq_len);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(KVF8_E_INVALID, "workspace of %zu bytes is too small, %zu needed", workspace_bytes, need);

@@ -67,6 +67,7 @@ struct DecodeArgs {
     int32_t out_bf16;
 };
 // Number of splits and chunk length the decode uses for this shape.
+constexpr int kDecodeThreads = 256;   // threads per decode workgroup (4 waves)
 void decode_plan(int32_t num_seqs, int32_t kv_heads, int32_t head_dim, int32_t block_size,
                  int32_t max_seq_len, int32_t *splits, int32_t *chunk_tokens);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
