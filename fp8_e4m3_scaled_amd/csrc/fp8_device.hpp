@@ -40,6 +40,21 @@ __device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) 
     return encode2(a, b) | (encode2(c, d) << 16);
 }
 
+// encode4 for values known not to be NaN (saturation still applies).
+__device__ __forceinline__ uint32_t encode4_finite(float a, float b, float c, float d) {
+    const float ca = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    const float cb = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    const float cc = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+    const float cd = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cc, cd, lo, true);
+}
+
+// True when any of the four codes in w is NaN (low seven bits all ones).
+__device__ __forceinline__ bool has_nan4(uint32_t w) {
+    return (((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u) != 0u;
+}
+
 // Multiply a bf16 value by the reciprocal scale; a NaN input keeps its own
 // sign (the sign of a NaN produced by an arithmetic operation is not fixed
 // by IEEE 754).

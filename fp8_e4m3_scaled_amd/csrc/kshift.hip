@@ -25,6 +25,8 @@ namespace kvf8 {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kRunsUnroll = 2;            // (slot, head) items in flight per lane
+constexpr int64_t kRunsMaxWgs = 4096;     // 16 workgroups per CU
 
 struct Table {
     float c[128];
@@ -45,72 +47,134 @@ __device__ __forceinline__ void load_table(Table &lds, const KShiftArgs &a) {
 }
 
 // Rotate one pair of codes; returns the two new codes (c0 in bits 0-7, c1 in 8-15).
-__device__ __forceinline__ uint32_t rotate_pair(float x0, float x1, float cf, float sf) {
+__device__ __forceinline__ uint32_t rotate_pair(float x0, float x1, double c, double s) {
 #pragma clang fp contract(off)
     if (__builtin_isnan(x0) || __builtin_isnan(x1)) return 0x7F7Fu;
-    const double c = (double)cf, s = (double)sf;
     const double a = (double)x0, b = (double)x1;
     const double y0 = a * c - b * s;
     const double y1 = a * s + b * c;
     return encode2((float)y0, (float)y1);
 }
 
-__global__ __launch_bounds__(kThreads) void kshift_runs(KShiftArgs a) {
-    __shared__ Table tab;
-    load_table(tab, a);
-    const int D = a.head_dim, BS = a.block_size, H = a.kv_heads;
-    const int runs = a.neox ? a.rot_dim / 32 : a.rot_dim / 16;
-    const int64_t item = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t total = a.n_slots * H * runs;
-    if (item >= total) return;
-    const int r = (int)(item % runs);
-    const int h = (int)((item / runs) % H);
-    const int64_t si = item / ((int64_t)runs * H);
-    const int64_t slot = a.slots[si];
-    if (slot < 0 || slot >= a.pool_slots) return;     // skipped, never written
-    const int64_t blk = slot / BS;
-    const int t = (int)(slot - blk * BS);
-    uint8_t *tile = a.k_pool + (blk * H + h) * (int64_t)BS * D;
+// The same rotation for non-NaN inputs.  x1*s and x1*c are exact in fp64, so
+// fma(x0, c, -(x1*s)) rounds x0*c - x1*s once, exactly like the two products
+// followed by a rounded subtraction.
+__device__ __forceinline__ void rotate_finite(float x0, float x1, double c, double s, float &y0, float &y1) {
+#pragma clang fp contract(off)
+    const double a = (double)x0, b = (double)x1;
+    y0 = (float)__builtin_fma(a, c, -(b * s));
+    y1 = (float)__builtin_fma(a, s, b * c);
+}
 
-    if (a.neox) {
-        const int i0 = 16 * r;
-        u32x4 *pa = reinterpret_cast<u32x4 *>(tile + k_offset(t, i0, BS, D));
-        u32x4 *pb = reinterpret_cast<u32x4 *>(tile + k_offset(t, i0 + a.rot_dim / 2, BS, D));
-        const u32x4 wa = *pa, wb = *pb;
-        u32x4 oa, ob;
+// Run path.  Thread g works on run r = g mod RP (RP: runs per row rounded up to
+// a power of two; lanes with r >= runs idle) of the (slot, head) items
+// j = g / RP, g / RP + J, ... with J = grid threads / RP, so its rotary pairs
+// never change: their cos/sin are held in registers.  U items are loaded per
+// iteration to keep several 16-byte loads in flight per lane.
+template <bool NEOX, int U>
+__global__ __launch_bounds__(kThreads) void kshift_runs(KShiftArgs a, int rp_log2) {
+    constexpr int NP = NEOX ? 16 : 8;      // rotary pairs per run
+    const int D = a.head_dim, H = a.kv_heads;
+    const int bs_log2 = a.block_size == 32 ? 5 : 4;
+    const int runs = NEOX ? a.rot_dim / 32 : a.rot_dim / 16;
+    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int r = (int)(g & ((1 << rp_log2) - 1));
+    const int64_t nj = a.n_slots * H;
+    int64_t j = g >> rp_log2;
+    if (r >= runs || j >= nj) return;
+    const int64_t jstep = ((int64_t)gridDim.x * kThreads) >> rp_log2;
+    const bool small = nj <= 0x7FFFFFFF;
+
+    double cs[NP], sn[NP];
+    const int p0 = NEOX ? 16 * r : 8 * r;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const f32x2 a01 = codes_to_f32x2<false>(wa[w]), a23 = codes_to_f32x2<true>(wa[w]);
-            const f32x2 b01 = codes_to_f32x2<false>(wb[w]), b23 = codes_to_f32x2<true>(wb[w]);
-            const float xa[4] = {a01[0], a01[1], a23[0], a23[1]};
-            const float xb[4] = {b01[0], b01[1], b23[0], b23[1]};
-            uint32_t ca = 0, cb = 0;
+    for (int k = 0; k < NP; ++k) {
+        cs[k] = (double)a.cos_t[p0 + k];
+        sn[k] = (double)a.sin_t[p0 + k];
+    }
+    const int da = 16 * r;                      // first byte run: dims [16r, 16r+16)
+    const int db = da + a.rot_dim / 2;          // NEOX partner run
+
+    for (; j < nj; j += U * jstep) {
+        int64_t oa[U], ob[U];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int i = i0 + 4 * w + k;
-                const uint32_t y = rotate_pair(xa[k], xb[k], tab.c[i], tab.s[i]);
-                ca |= (y & 0xFFu) << (8 * k);
-                cb |= ((y >> 8) & 0xFFu) << (8 * k);
+        for (int u = 0; u < U; ++u) {
+            const int64_t jj = j + u * jstep;
+            oa[u] = -1;
+            if (jj < nj) {
+                int64_t si;
+                int h;
+                if (small) {
+                    si = (uint32_t)jj / (uint32_t)H;
+                    h = (int)((uint32_t)jj - (uint32_t)si * (uint32_t)H);
+                } else {
+                    si = jj / H;
+                    h = (int)(jj - si * H);
+                }
+                const int64_t slot = a.slots[si];
+                if (slot >= 0 && slot < a.pool_slots) {   // others are skipped, never written
+                    const int64_t blk = slot >> bs_log2;
+                    const int t = (int)(slot - (blk << bs_log2));
+                    const int64_t tile = ((blk * H + h) << bs_log2) * D;
+                    oa[u] = tile + k_offset(t, da, a.block_size, D);
+                    ob[u] = tile + k_offset(t, db, a.block_size, D);
+                }
             }
-            oa[w] = ca;
-            ob[w] = cb;
         }
-        *pa = oa;
-        *pb = ob;
-    } else {
-        const int d0 = 16 * r;           // eight (2i, 2i+1) pairs, i = d0/2 ..
-        u32x4 *pa = reinterpret_cast<u32x4 *>(tile + k_offset(t, d0, BS, D));
-        const u32x4 wa = *pa;
-        u32x4 oa;
+        u32x4 wa[U], wb[U];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const f32x2 a01 = codes_to_f32x2<false>(wa[w]), a23 = codes_to_f32x2<true>(wa[w]);
-            const int i = d0 / 2 + 2 * w;
-            const uint32_t y0 = rotate_pair(a01[0], a01[1], tab.c[i], tab.s[i]);
-            const uint32_t y1 = rotate_pair(a23[0], a23[1], tab.c[i + 1], tab.s[i + 1]);
-            oa[w] = (y0 & 0xFFFFu) | (y1 << 16);
+        for (int u = 0; u < U; ++u) {
+            if (oa[u] >= 0) {
+                wa[u] = *reinterpret_cast<const u32x4 *>(a.k_pool + oa[u]);
+                if (NEOX) wb[u] = *reinterpret_cast<const u32x4 *>(a.k_pool + ob[u]);
+            }
         }
-        *pa = oa;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (oa[u] < 0) continue;
+            u32x4 na, nb;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t A = wa[u][w], B = NEOX ? wb[u][w] : 0u;
+                const f32x2 a01 = codes_to_f32x2<false>(A), a23 = codes_to_f32x2<true>(A);
+                if (NEOX) {
+                    const f32x2 b01 = codes_to_f32x2<false>(B), b23 = codes_to_f32x2<true>(B);
+                    const float xa[4] = {a01[0], a01[1], a23[0], a23[1]};
+                    const float xb[4] = {b01[0], b01[1], b23[0], b23[1]};
+                    if (!(has_nan4(A) || has_nan4(B))) {
+                        float y0[4], y1[4];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            rotate_finite(xa[k], xb[k], cs[4 * w + k], sn[4 * w + k], y0[k], y1[k]);
+                        na[w] = encode4_finite(y0[0], y0[1], y0[2], y0[3]);
+                        nb[w] = encode4_finite(y1[0], y1[1], y1[2], y1[3]);
+                    } else {
+                        uint32_t ca = 0, cb = 0;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const uint32_t y = rotate_pair(xa[k], xb[k], cs[4 * w + k], sn[4 * w + k]);
+                            ca |= (y & 0xFFu) << (8 * k);
+                            cb |= ((y >> 8) & 0xFFu) << (8 * k);
+                        }
+                        na[w] = ca;
+                        nb[w] = cb;
+                    }
+                } else {
+                    if (!has_nan4(A)) {
+                        float p0, q0, p1, q1;
+                        rotate_finite(a01[0], a01[1], cs[2 * w], sn[2 * w], p0, q0);
+                        rotate_finite(a23[0], a23[1], cs[2 * w + 1], sn[2 * w + 1], p1, q1);
+                        na[w] = encode4_finite(p0, q0, p1, q1);
+                    } else {
+                        const uint32_t y0 = rotate_pair(a01[0], a01[1], cs[2 * w], sn[2 * w]);
+                        const uint32_t y1 = rotate_pair(a23[0], a23[1], cs[2 * w + 1], sn[2 * w + 1]);
+                        na[w] = (y0 & 0xFFFFu) | (y1 << 16);
+                    }
+                }
+            }
+            *reinterpret_cast<u32x4 *>(a.k_pool + oa[u]) = na;
+            if (NEOX) *reinterpret_cast<u32x4 *>(a.k_pool + ob[u]) = nb;
+        }
     }
 }
 
@@ -135,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void kshift_pairs(KShiftArgs a) {
     uint8_t *b0 = tile + k_offset(t, d0, BS, D);
     uint8_t *b1 = tile + k_offset(t, d1, BS, D);
     const f32x2 x = codes_to_f32x2<false>((uint32_t)*b0 | ((uint32_t)*b1 << 8));
-    const uint32_t y = rotate_pair(x[0], x[1], tab.c[p], tab.s[p]);
+    const uint32_t y = rotate_pair(x[0], x[1], (double)tab.c[p], (double)tab.s[p]);
     *b0 = (uint8_t)(y & 0xFF);
     *b1 = (uint8_t)(y >> 8);
 }
@@ -144,14 +208,26 @@ __global__ __launch_bounds__(kThreads) void kshift_pairs(KShiftArgs a) {
 
 hipError_t launch_kshift(const KShiftArgs &a, hipStream_t stream) {
     const bool runs = a.neox ? (a.rot_dim % 32 == 0) : (a.rot_dim % 16 == 0);
-    const int64_t per_row = runs ? (a.neox ? a.rot_dim / 32 : a.rot_dim / 16) : a.rot_dim / 2;
-    const int64_t total = a.n_slots * a.kv_heads * per_row;
+    if (runs) {
+        const int per_row = a.neox ? a.rot_dim / 32 : a.rot_dim / 16;
+        int rp_log2 = 0;
+        while ((1 << rp_log2) < per_row) ++rp_log2;
+        const int64_t threads = (a.n_slots * a.kv_heads) << rp_log2;
+        int64_t wgs = (threads + kThreads - 1) / kThreads;
+        if (wgs > kRunsMaxWgs) wgs = kRunsMaxWgs;     // then each thread loops
+        if (wgs < 1) wgs = 1;
+        if (a.neox)
+            hipLaunchKernelGGL((kshift_runs<true, kRunsUnroll>), dim3((unsigned)wgs), dim3(kThreads), 0, stream,
+                               a, rp_log2);
+        else
+            hipLaunchKernelGGL((kshift_runs<false, kRunsUnroll>), dim3((unsigned)wgs), dim3(kThreads), 0, stream,
+                               a, rp_log2);
+        return hipGetLastError();
+    }
+    const int64_t total = a.n_slots * a.kv_heads * (a.rot_dim / 2);
     const int64_t wgs = (total + kThreads - 1) / kThreads;
     if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (runs)
-        hipLaunchKernelGGL(kshift_runs, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(kshift_pairs, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(kshift_pairs, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
