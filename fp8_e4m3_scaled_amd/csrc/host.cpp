@@ -392,6 +392,9 @@ kvf8_status paged_attn_decode(kvf8_cache *c, int32_t layer, const uint16_t *q_bf
     a.splits = splits;
     a.chunk_tokens = chunk;
     a.qk_scale = c->k_scale[layer] * sm_scale * 1.4426950408889634f;
+    if (!(std::isfinite(a.qk_scale) && a.qk_scale != 0.0f))
+        return fail(KVF8_E_SCALE, "k_scale * sm_scale * log2(e) = %g is not a finite nonzero fp32 factor",
+                    (double)a.qk_scale);
     a.v_scale = c->v_scale[layer];
     a.out_bf16 = out_dtype == KVF8_DTYPE_BF16;
     hipError_t e = kvf8::launch_decode(a, static_cast<hipStream_t>(stream));
@@ -442,6 +445,9 @@ kvf8_status paged_attn_prefill_chunk(kvf8_cache *c, int32_t layer, const uint16_
     a.block_size = c->block_size;
     a.max_q_len = max_q_len;
     a.qk_scale = c->k_scale[layer] * sm_scale * 1.4426950408889634f;
+    if (!(std::isfinite(a.qk_scale) && a.qk_scale != 0.0f))
+        return fail(KVF8_E_SCALE, "k_scale * sm_scale * log2(e) = %g is not a finite nonzero fp32 factor",
+                    (double)a.qk_scale);
     a.v_scale = c->v_scale[layer];
     a.out_bf16 = out_dtype == KVF8_DTYPE_BF16;
     hipError_t e = kvf8::launch_prefill(a, static_cast<hipStream_t>(stream));

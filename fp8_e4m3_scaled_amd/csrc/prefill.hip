@@ -17,8 +17,9 @@
 //   * S^T[key][row] = K Q^T on v_mfma_f32_16x16x32_bf16; its output is the
 //     B operand of O^T[d][row] += V^T P^T on v_mfma_f32_16x16x32_f16;
 //   * online softmax per row in the log2 domain with the same lazy reference
-//     as the decode; causal masking only on steps that reach the tile's
-//     first query position.
+//     as the decode, P = exp2(fma(s, |qk|, -max)) from the raw MFMA scores;
+//     causal masking only on steps that reach the tile's first query
+//     position; the row sums come from one more MFMA with an all-ones V.
 // The next step's tiles are loaded into registers while the current one is
 // computed, then written to the other LDS buffer.
 
@@ -34,6 +35,7 @@ constexpr int kStep = 32;              // keys per step (two 16-key tiles)
 constexpr int kNR = 2;                 // 16-row MFMA tiles per wave
 constexpr int kRows = kWaves * kNR * 16;
 constexpr float kLazy = 8.0f;
+constexpr float kNoMax = -1.0e30f;     // running-max sentinel (finite: see the accumulators)
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -110,7 +112,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     const uint32_t last_block = (uint32_t)(a.num_blocks - 1);
     const int32_t *table = a.block_tables + (int64_t)b * a.max_blocks;
 
-    // ---- Q^T operands of this wave's two row tiles; lane (n, g) holds row n
+    // ---- Q^T operands of this wave's two row tiles; lane (n, g) holds row n.
+    // A negative qk_scale is folded into Q (an exact sign flip of every bf16),
+    // so the MFMA yields s / |qk_scale| * qk_scale's sign and the softmax works
+    // with qk = |qk_scale| > 0.
+    const uint32_t qsign = a.qk_scale < 0.0f ? 0x80008000u : 0u;
+    const float qk = fabsf(a.qk_scale);
     bf16x8 qb[kNR][KK];
     int row_pos[kNR];          // causal limit of lane-row n in tile j (key <= row_pos)
     bool row_live[kNR];
@@ -127,19 +134,31 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         for (int kk = 0; kk < KK; ++kk) {
             uint4 w = make_uint4(0, 0, 0, 0);
             if (row_live[j]) w = *reinterpret_cast<const uint4 *>(qrow + 8 * kk);
+            w.x ^= qsign;
+            w.y ^= qsign;
+            w.z ^= qsign;
+            w.w ^= qsign;
             qb[j][kk] = __builtin_bit_cast(bf16x8, w);
         }
     }
 
+    // run_max starts at a finite sentinel far below any score, so that
+    // exp2(s*qk - run_max) of a masked score (-inf) is 0 without a select and
+    // the first rescale factor exp2(sentinel - ref) is 0.  The row sums are
+    // accumulated by the MFMA with an all-ones A operand (sum_k P[row][k] in
+    // every output dim), from the same f16 P as the numerator.
     f32x4 acc[kNR][MT];
-    float run_max[kNR], run_sum[kNR];
+    f32x4 lsum[kNR];
+    float run_max[kNR];
 #pragma unroll
     for (int j = 0; j < kNR; ++j) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        run_max[j] = -__builtin_inff();
-        run_sum[j] = 0.0f;
+        lsum[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        run_max[j] = kNoMax;
     }
+    const f16x8 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                        (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
 
     auto blocks_of = [&](int p, uint32_t &b0, uint32_t &b1) {
         const int e0 = min(p, total - 1) / BS;
@@ -226,11 +245,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
                 for (int kk = 0; kk < KK; ++kk)
                     sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t][kk], qb[j][kk], sc[t], 0, 0, 0);
             }
-            float x[8];
+            float x[8];                                    // raw scores, scaled inside exp2
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[4 * t + i] = sc[t][i] * a.qk_scale;
+                for (int i = 0; i < 4; ++i) x[4 * t + i] = sc[t][i];
             if (diag || tail) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
@@ -243,25 +262,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx *= qk;
             if (__any(mx > run_max[j] + kLazy)) {
                 const float ref = fmaxf(run_max[j], mx);
-                const float alpha = ref == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f(run_max[j] - ref);
-                run_sum[j] *= alpha;
+                const float alpha = __builtin_amdgcn_exp2f(run_max[j] - ref);
+                lsum[j] *= alpha;
 #pragma unroll
                 for (int t = 0; t < MT; ++t) acc[j][t] *= alpha;
                 run_max[j] = ref;
             }
+            const float nm = -run_max[j];
             float pr[8];
-            float psum = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                // a row with no key yet (ref still -inf) has every x masked: p = 0
-                pr[i] = x[i] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(x[i] - run_max[j]);
-                psum += pr[i];
-            }
-            run_sum[j] += psum;
+            for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], qk, nm));
             pb[j] = f16x8{(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3],
                           (_Float16)pr[4], (_Float16)pr[5], (_Float16)pr[6], (_Float16)pr[7]};
+            lsum[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[j], lsum[j], 0, 0, 0);
         }
         // ---- O^T += V^T P^T, V operands converted once for both row tiles
 #pragma unroll
@@ -280,9 +296,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     // ---- normalize and write: lane (n, g) holds rows n of its tiles, dims (D/16)(4g+r)+t
 #pragma unroll
     for (int j = 0; j < kNR; ++j) {
-        float l = run_sum[j];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        const float l = lsum[j][0];          // every output dim of the ones product holds the row sum
         if (!row_live[j]) continue;
         const int r = (wave * kNR + j) * 16 + m;
         const int tok = i0 + r / G;

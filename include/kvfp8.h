@@ -197,7 +197,9 @@ size_t paged_attn_decode_workspace(const kvf8_cache *cache, int32_t num_seqs,
  * seq_lens (device): int32 [num_seqs], each 0 .. max_seq_len and at most
  *   max_blocks_per_seq * block_size.
  * max_seq_len (host): upper bound of seq_lens, sizes the launch.
- * sm_scale: softmax scale, finite and > 0 (usually 1/sqrt(head_dim)).
+ * sm_scale: softmax scale, finite and > 0 (usually 1/sqrt(head_dim)); the
+ *   fp32 factor k_scale * sm_scale * log2(e) must be finite and nonzero
+ *   (else KVF8_E_SCALE).
  * out (device): [num_seqs][num_q_heads][head_dim], fp32 or bf16 (out_dtype).
  * workspace (device): at least paged_attn_decode_workspace(...) bytes,
  *   used as scratch by this call only; may be NULL when that is 0.
@@ -230,6 +232,8 @@ kvf8_status paged_attn_decode(kvf8_cache *cache, int32_t layer, const uint16_t *
  *   max_blocks_per_seq * block_size (keys past the table row are never
  *   read).  max_q_len / max_ctx_len (host): upper bounds of the chunk lengths
  *   and context lengths, size the launch.
+ * sm_scale: as in paged_attn_decode (KVF8_E_SCALE when k_scale * sm_scale *
+ *   log2(e) is 0 or not finite in fp32).
  * out (device): [total_q][num_q_heads][head_dim], fp32 or bf16.
  */
 kvf8_status paged_attn_prefill_chunk(kvf8_cache *cache, int32_t layer, const uint16_t *q_bf16,

@@ -198,6 +198,24 @@ def test_compute_calls_fail_their_host_checks():
         kv.kv_cache_free(c)
 
 
+def test_score_factor_must_be_a_usable_fp32():
+    """k_scale * sm_scale * log2(e) must be finite and nonzero in fp32: a factor
+    that underflows to 0 or overflows is refused before any launch."""
+    for ks, sm in [(1e-38, 1e-10), (1e38, 1e10)]:
+        c = _cache(h=2, d=64, ks=[ks, ks], vs=[1.0, 1.0])
+        try:
+            with pytest.raises(kv.KvF8Error) as ei:
+                kv.paged_attn_decode(c, 0, 1 << 30, 4, 1 << 30, 4, 1 << 30, 2, 64, sm, 1 << 30,
+                                     kv.DTYPE_F32, None, 0, 0)
+            assert ei.value.status == kv.E_SCALE
+            with pytest.raises(kv.KvF8Error) as ei:
+                kv.paged_attn_prefill_chunk(c, 0, 1 << 30, 4, 1 << 30, 1 << 30, 1 << 30, 4, 1, 8, 8,
+                                            16, sm, 1 << 30, kv.DTYPE_F32, 0)
+            assert ei.value.status == kv.E_SCALE
+        finally:
+            kv.kv_cache_free(c)
+
+
 def test_workspace_size_is_consistent():
     c = _cache(h=2, d=64)
     try:
