@@ -428,6 +428,13 @@ kvf8_status paged_attn_prefill_chunk(kvf8_cache *c, int32_t layer, const uint16_
         return fail(KVF8_E_INVALID, "q, cu_q_lens, context_lens, block_tables and out must be non-NULL");
     if ((reinterpret_cast<uintptr_t>(q_bf16) % 16) != 0)
         return fail(KVF8_E_INVALID, "q must be 16-byte aligned");
+    {   // one workgroup per (sequence, kv head, 128-row query tile), pairs padded to a multiple of 8
+        const int64_t tok_per_tile = kvf8::kPrefillRows / (num_q_heads / c->kv_heads);
+        const int64_t units = ((int64_t)max_q_len + tok_per_tile - 1) / tok_per_tile *
+                              ((((int64_t)num_seqs * c->kv_heads) + 7) / 8 * 8);
+        if (units * kvf8::kPrefillThreads >= ((int64_t)1 << 32))
+            return fail(KVF8_E_UNSUPPORTED, "%lld prefill workgroups exceed one launch", (long long)units);
+    }
     kvf8::PrefillArgs a{};
     a.q = q_bf16;
     a.k_pool = k_pool_of(c, layer);

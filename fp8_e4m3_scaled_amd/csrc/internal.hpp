@@ -68,6 +68,8 @@ struct DecodeArgs {
 };
 // Number of splits and chunk length the decode uses for this shape.
 constexpr int kDecodeThreads = 256;   // threads per decode workgroup (4 waves)
+constexpr int kPrefillThreads = 256;  // threads per prefill workgroup (4 waves)
+constexpr int kPrefillRows = 128;     // (query token, head) rows per prefill workgroup
 void decode_plan(int32_t num_seqs, int32_t kv_heads, int32_t head_dim, int32_t block_size,
                  int32_t max_seq_len, int32_t *splits, int32_t *chunk_tokens);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
@@ -105,6 +107,7 @@ struct PrefillArgs {
     int32_t head_dim;
     int32_t block_size;
     int32_t max_q_len;
+    int32_t q_tiles;         // query-row tiles per (sequence, kv head), set by the launcher
     float qk_scale;          // k_scale * sm_scale * log2(e)
     float v_scale;
     int32_t out_bf16;

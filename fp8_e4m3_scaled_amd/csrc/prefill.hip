@@ -31,11 +31,16 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+static_assert(kThreads == kPrefillThreads, "host launch checks assume this workgroup size");
 constexpr int kStep = 32;              // keys per step (two 16-key tiles)
 constexpr int kNR = 2;                 // 16-row MFMA tiles per wave
 constexpr int kRows = kWaves * kNR * 16;
+static_assert(kRows == kPrefillRows, "host launch checks assume this tile height");
 constexpr float kLazy = 8.0f;
-constexpr float kNoMax = -1.0e30f;     // running-max sentinel (finite: see the accumulators)
+constexpr float kNoMax = -1.0e30f;
+constexpr int kUnitScale = 127;          // E8M0 exponent of 1.0 for the scaled fp8 MFMA
+
+typedef __attribute__((ext_vector_type(8))) int v8i;     // running-max sentinel (finite: see the accumulators)
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -53,10 +58,32 @@ struct StepLds {
 
 // Per-thread share of one step's global->LDS copy: 16-byte chunks.
 template <int D>
-struct CopyRegs {
+struct CopyShare {
     static constexpr int CHUNKS = StepLds<D>::BYTES / 16 / kThreads;   // 2 (D=128), 4 (D=256), 1 (D=64)
-    u32x4 w[CHUNKS];
 };
+
+// K/V steps in LDS: the one being computed and kStages-1 in flight.
+constexpr int kStages = 4;
+
+// A uniform-index read of read-only memory through the constant address
+// space, so that it becomes a scalar load.
+__device__ __forceinline__ int32_t load_uniform(const int32_t *p, int i) {
+    return ((const __attribute__((address_space(4))) int32_t *)p)[i];
+}
+
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane i writes bytes [16i, 16i+16) of the
+// wave-uniform destination.  Counted by vmcnt like any load.
+__device__ __forceinline__ void load_to_lds16(const void *src, uint8_t *wave_dst) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)wave_dst, 16, 0, 0);
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 // Chunk c of a step (c in [0, 4*D)): tile kind (K/V), 16-key tile t, offset.
 // K tile t: 4 quarters of 16 keys x D/4 bytes; in the cache quarter q of the
@@ -84,17 +111,26 @@ __device__ __forceinline__ const uint8_t *chunk_src(int c, const uint8_t *k_pool
 
 template <int D, int BS>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
-    constexpr int KK = D / 32;
+    constexpr int NC = D >= 128 ? D / 128 : 1;   // 128-dim K chunks per tile (D = 64: one, zero-padded)
     constexpr int MT = D / 16;
     constexpr int Q4 = D / 4;
     constexpr int NW = D / 16;
     constexpr int TILE = StepLds<D>::TILE;
-    constexpr int CH = CopyRegs<D>::CHUNKS;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][StepLds<D>::BYTES];
+    constexpr int CH = CopyShare<D>::CHUNKS;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kStages][StepLds<D>::BYTES];
 
-    const int qt = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z;
+    // Workgroups go to the 8 XCDs round-robin by linear id; every query tile
+    // of pair p = seq * kv_heads + kv_head runs on XCD p % 8, the pair's tiles
+    // dispatched together, so one XCD's L2 serves all reads of the pair's K/V
+    // while its tiles walk the keys side by side.  Pairs are padded to a
+    // multiple of 8; padding ids exit at once.
+    const uint32_t hid = blockIdx.x;
+    const uint32_t kx = hid >> 3;
+    const int pair = (int)(kx / (uint32_t)a.q_tiles) * 8 + (int)(hid & 7);
+    const int qt = (int)(kx % (uint32_t)a.q_tiles);
+    if (pair >= a.num_seqs * a.kv_heads) return;
+    const int kvh = pair % a.kv_heads;
+    const int b = pair / a.kv_heads;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int m = lane & 15;
@@ -112,13 +148,23 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     const uint32_t last_block = (uint32_t)(a.num_blocks - 1);
     const int32_t *table = a.block_tables + (int64_t)b * a.max_blocks;
 
-    // ---- Q^T operands of this wave's two row tiles; lane (n, g) holds row n.
-    // A negative qk_scale is folded into Q (an exact sign flip of every bf16),
-    // so the MFMA yields s / |qk_scale| * qk_scale's sign and the softmax works
-    // with qk = |qk_scale| > 0.
-    const uint32_t qsign = a.qk_scale < 0.0f ? 0x80008000u : 0u;
+    // ---- Q^T operands of this wave's two row tiles; lane (n, g) holds quarter
+    // g of row n's dims (byte e = dim g*D/4 + e, the K tile's order).
+    //
+    // S^T = K Q^T runs on the fp8 MFMA with the K codes as they are in the
+    // cache.  Q is split exactly into two E4M3 terms per row: with 2^e the
+    // power of two that puts the row's max |q| in [128, 256),
+    //   y = q * 2^e,  hi = E4M3(y),  lo = E4M3(y - hi),
+    // and hi + lo == y for every element with |y| >= 1/4 (a bf16 significand
+    // has 8 bits, E4M3 keeps 4, and the remainder of the round-to-nearest is
+    // a 4-bit multiple of y's last place); smaller elements are off by at
+    // most 2^-10, i.e. 2^-17 of the row max.  So K.(hi + lo) = 2^e (K.q) to
+    // fp32 accumulation, and 2^-e goes into the row's exp2 factor.  A
+    // negative qk_scale flips the sign of y (exact).
     const float qk = fabsf(a.qk_scale);
-    bf16x8 qb[kNR][KK];
+    const float qsgn = a.qk_scale < 0.0f ? -1.0f : 1.0f;
+    v8i qh[kNR][NC], ql[kNR][NC];
+    float qk_row[kNR];
     int row_pos[kNR];          // causal limit of lane-row n in tile j (key <= row_pos)
     bool row_live[kNR];
 #pragma unroll
@@ -130,16 +176,67 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         row_live[j] = r < tok_per_tile * G && tok < q_len;
         row_pos[j] = ctx + tok;
         const uint16_t *qrow = a.q + ((int64_t)(q0 + (row_live[j] ? tok : 0)) * a.q_heads + head) * D + g * (D / 4);
+        float y[D / 4];
+        float amax = 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
+        for (int kk = 0; kk < D / 32; ++kk) {
             uint4 w = make_uint4(0, 0, 0, 0);
             if (row_live[j]) w = *reinterpret_cast<const uint4 *>(qrow + 8 * kk);
-            w.x ^= qsign;
-            w.y ^= qsign;
-            w.z ^= qsign;
-            w.w ^= qsign;
-            qb[j][kk] = __builtin_bit_cast(bf16x8, w);
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                y[8 * kk + 2 * e] = __uint_as_float(ww[e] << 16);
+                y[8 * kk + 2 * e + 1] = __uint_as_float(ww[e] & 0xFFFF0000u);
+            }
         }
+        int bad = 0;                        // a NaN or infinite element in the row
+#pragma unroll
+        for (int i = 0; i < D / 4; ++i) {
+            amax = fmaxf(amax, fabsf(y[i]));
+            bad |= !__builtin_isfinite(y[i]);
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        bad |= __shfl_xor(bad, 16);
+        bad |= __shfl_xor(bad, 32);
+        int ex = 0;
+        if (!bad && amax > 0.0f) {
+            int E;
+            (void)frexpf(amax, &E);         // amax = f * 2^E, f in [0.5, 1)
+            ex = 8 - E;
+        }
+        qk_row[j] = ldexpf(qk, -ex);
+        const float mul = ldexpf(qsgn, ex);
+        uint32_t hw[D / 16], lw[D / 16];
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) {
+            float v[4], hv[4], rv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = y[4 * i + e] * mul;     // exact: a power of two
+            int h = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+            h = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], h, true);
+            const f32x2 b01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+            const f32x2 b23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+            hv[0] = b01[0]; hv[1] = b01[1]; hv[2] = b23[0]; hv[3] = b23[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rv[e] = v[e] - hv[e];          // exact
+            int l = __builtin_amdgcn_cvt_pk_fp8_f32(rv[0], rv[1], 0, false);
+            l = __builtin_amdgcn_cvt_pk_fp8_f32(rv[2], rv[3], l, true);
+            hw[i] = (uint32_t)h;
+            lw[i] = (uint32_t)l;
+        }
+        if (bad) {                          // a non-finite q makes the whole row NaN
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i) hw[i] = 0x7F7F7F7Fu;
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int wi = 8 * c + i;
+                qh[j][c][i] = wi < D / 16 ? (int)hw[wi < D / 16 ? wi : 0] : 0;
+                ql[j][c][i] = wi < D / 16 ? (int)lw[wi < D / 16 ? wi : 0] : 0;
+            }
     }
 
     // run_max starts at a finite sentinel far below any score, so that
@@ -160,41 +257,46 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     const f16x8 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
                         (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
 
+    // Block ids come through the constant address space: the index is uniform,
+    // so these are scalar loads (lgkmcnt), not vector loads that would make
+    // the compiler wait for the in-flight LDS transfers.
     auto blocks_of = [&](int p, uint32_t &b0, uint32_t &b1) {
-        const int e0 = min(p, total - 1) / BS;
-        const int e1 = min(p + 16, total - 1) / BS;
-        b0 = min((uint32_t)table[e0], last_block);
-        b1 = min((uint32_t)table[e1], last_block);
+        const int e0 = __builtin_amdgcn_readfirstlane(min(p, total - 1) / BS);
+        const int e1 = __builtin_amdgcn_readfirstlane(min(p + 16, total - 1) / BS);
+        b0 = min((uint32_t)load_uniform(table, e0), last_block);
+        b1 = min((uint32_t)load_uniform(table, e1), last_block);
     };
-    auto fetch = [&](CopyRegs<D> &r, int p) {
+    // Step st's K/V tiles go straight from global memory into LDS stage
+    // st % kStages (global_load_lds_dwordx4: lane i of a wave writes bytes
+    // 16i.. of the wave's 1 KiB).  Steps past the last one re-read the
+    // sequence's last block (blocks_of clamps), so every step issues the same
+    // CH loads and the vmcnt arithmetic below holds.
+    auto issue = [&](int st) {
+        const int p = st * kStep;
         uint32_t b0, b1;
         blocks_of(p, b0, b1);
+        uint8_t *stage = lds[st % kStages];
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const int c = threadIdx.x + i * kThreads;
-            r.w[i] = *reinterpret_cast<const u32x4 *>(chunk_src<D, BS>(c, a.k_pool, a.v_pool, b0, b1,
-                                                                         a.kv_heads, kvh, p));
-        }
-    };
-    auto stash = [&](const CopyRegs<D> &r, int buf) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = threadIdx.x + i * kThreads;
-            *reinterpret_cast<u32x4 *>(&lds[buf][c * 16]) = r.w[i];
+            load_to_lds16(chunk_src<D, BS>(c, a.k_pool, a.v_pool, b0, b1, a.kv_heads, kvh, p),
+                          stage + (c - lane) * 16);
         }
     };
 
-    CopyRegs<D> cr;
-    if (nsteps > 0) {
-        fetch(cr, 0);
-        stash(cr, 0);
-    }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i) issue(i);
     const int first_row_pos = ctx + i0;
     for (int s = 0; s < nsteps; ++s) {
         const int p = s * kStep;
-        const int buf = s & 1;
-        if (s + 1 < nsteps) fetch(cr, p + kStep);
+        const int buf = s % kStages;
+        wait_vmcnt<(kStages - 2) * CH>();   // this wave's share of step s has landed
+        // Everyone's share has, and every wave is done with step s-1's stage.
+        // A bare s_barrier: the workgroup release fence of __syncthreads would
+        // also wait for the transfers still in flight.  The ds_reads of step
+        // s-1 were consumed by its MFMAs, so none is pending here.
+        asm volatile("s_barrier" ::: "memory");
+        issue(s + kStages - 1);
 
         // ---- operands of this step from LDS (same lane mapping as the decode's loads)
         uint32_t kw[2][NW], vw[2][NW];
@@ -223,17 +325,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
                 for (int i = 0; i < NW; ++i) vw[t][i] &= keep;
             }
         }
-        // K operands converted once for both row tiles
-        bf16x8 ka[2][KK];
+        // K operands: the lane's D/4 codes of each tile, as they are
+        v8i ka[2][NC];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const uint32_t w0 = kw[t][2 * kk], w1 = kw[t][2 * kk + 1];
-                const bf16x2 e0 = codes_to_bf16x2<false>(w0), e1 = codes_to_bf16x2<true>(w0);
-                const bf16x2 e2 = codes_to_bf16x2<false>(w1), e3 = codes_to_bf16x2<true>(w1);
-                ka[t][kk] = bf16x8{e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
-            }
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int wi = 8 * c + i;
+                    ka[t][c][i] = wi < NW ? (int)kw[t][wi < NW ? wi : 0] : 0;
+                }
         f16x8 pb[kNR];
 #pragma unroll
         for (int j = 0; j < kNR; ++j) {
@@ -242,8 +344,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             for (int t = 0; t < 2; ++t) {
                 sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < KK; ++kk)
-                    sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t][kk], qb[j][kk], sc[t], 0, 0, 0);
+                for (int c = 0; c < NC; ++c) {
+                    sc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[t][c], qh[j][c], sc[t], 0, 0,
+                                                                             0, kUnitScale, 0, kUnitScale);
+                    sc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[t][c], ql[j][c], sc[t], 0, 0,
+                                                                             0, kUnitScale, 0, kUnitScale);
+                }
             }
             float x[8];                                    // raw scores, scaled inside exp2
 #pragma unroll
@@ -262,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            mx *= qk;
+            mx *= qk_row[j];
             if (__any(mx > run_max[j] + kLazy)) {
                 const float ref = fmaxf(run_max[j], mx);
                 const float alpha = __builtin_amdgcn_exp2f(run_max[j] - ref);
@@ -274,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             const float nm = -run_max[j];
             float pr[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], qk, nm));
+            for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], qk_row[j], nm));
             pb[j] = f16x8{(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3],
                           (_Float16)pr[4], (_Float16)pr[5], (_Float16)pr[6], (_Float16)pr[7]};
             lsum[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[j], lsum[j], 0, 0, 0);
@@ -289,9 +395,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             for (int j = 0; j < kNR; ++j)
                 acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[j], acc[j][t], 0, 0, 0);
         }
-        if (s + 1 < nsteps) stash(cr, buf ^ 1);
-        __syncthreads();
     }
+    wait_vmcnt<0>();    // no LDS write may still be in flight when the workgroup ends
 
     // ---- normalize and write: lane (n, g) holds rows n of its tiles, dims (D/16)(4g+r)+t
 #pragma unroll
@@ -323,8 +428,10 @@ hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
     const int tok_per_tile = kRows / G;
     const int tiles = (a.max_q_len + tok_per_tile - 1) / tok_per_tile;
     if (tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_kernel<D, BS>), dim3(tiles, a.kv_heads, a.num_seqs), dim3(kThreads), 0,
-                       stream, a);
+    PrefillArgs la = a;
+    la.q_tiles = tiles;
+    const uint32_t units = (uint32_t)tiles * (uint32_t)(((a.num_seqs * a.kv_heads + 7) >> 3) << 3);
+    hipLaunchKernelGGL((prefill_kernel<D, BS>), dim3(units), dim3(kThreads), 0, stream, la);
     return hipGetLastError();
 }
 
