@@ -78,6 +78,18 @@ __device__ __forceinline__ void load_to_lds16(const void *src, uint8_t *wave_dst
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)wave_dst, 16, 0, 0);
 }
 
+// max(v, v of lane ^ 16) and max(v, v of lane ^ 32) with the gfx950 row
+// swaps (full-rate VALU, no LDS round trip): with both operands the same
+// register, each lane gets back its own value and its partner's.
+__device__ __forceinline__ float max_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Wait until at most N of this wave's vector-memory loads are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -336,51 +348,66 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
                     const int wi = 8 * c + i;
                     ka[t][c][i] = wi < NW ? (int)kw[t][wi < NW ? wi : 0] : 0;
                 }
-        f16x8 pb[kNR];
+        // ---- S^T for both row tiles, then their row maxima, then one wave
+        // vote for the lazy rescale: straight-line code for both tiles between
+        // the vote's branches, so their latency chains can interleave.
+        f32x4 sc[kNR][2];
 #pragma unroll
-        for (int j = 0; j < kNR; ++j) {
-            f32x4 sc[2];
+        for (int j = 0; j < kNR; ++j)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                sc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    sc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[t][c], qh[j][c], sc[t], 0, 0,
-                                                                             0, kUnitScale, 0, kUnitScale);
-                    sc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[t][c], ql[j][c], sc[t], 0, 0,
-                                                                             0, kUnitScale, 0, kUnitScale);
+                    sc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[t][c], qh[j][c], sc[j][t], 0, 0,
+                                                                                0, kUnitScale, 0, kUnitScale);
+                    sc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[t][c], ql[j][c], sc[j][t], 0, 0,
+                                                                                0, kUnitScale, 0, kUnitScale);
                 }
             }
-            float x[8];                                    // raw scores, scaled inside exp2
+        float x[kNR][8];                                   // raw scores, scaled inside exp2
+        float mx[kNR];
+        bool grow = false;
+#pragma unroll
+        for (int j = 0; j < kNR; ++j) {
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[4 * t + i] = sc[t][i];
+                for (int i = 0; i < 4; ++i) x[j][4 * t + i] = sc[j][t][i];
             if (diag || tail) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int key = p + 16 * t + 4 * g + i;
-                        if (key > row_pos[j] || key >= total) x[4 * t + i] = -__builtin_inff();
+                        if (key > row_pos[j] || key >= total) x[j][4 * t + i] = -__builtin_inff();
                     }
             }
-            float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            mx *= qk_row[j];
-            if (__any(mx > run_max[j] + kLazy)) {
-                const float ref = fmaxf(run_max[j], mx);
+            float m8 = fmaxf(fmaxf(fmaxf(x[j][0], x[j][1]), fmaxf(x[j][2], x[j][3])),
+                             fmaxf(fmaxf(x[j][4], x[j][5]), fmaxf(x[j][6], x[j][7])));
+            m8 = max_xor16(m8);            // the row's four k-groups: lanes n, n^16, n^32, n^48
+            m8 = max_xor32(m8);
+            mx[j] = m8 * qk_row[j];
+            grow |= mx[j] > run_max[j] + kLazy;
+        }
+        if (__any(grow)) {
+#pragma unroll
+            for (int j = 0; j < kNR; ++j) {
+                const float ref = fmaxf(run_max[j], mx[j]);
                 const float alpha = __builtin_amdgcn_exp2f(run_max[j] - ref);
                 lsum[j] *= alpha;
 #pragma unroll
                 for (int t = 0; t < MT; ++t) acc[j][t] *= alpha;
                 run_max[j] = ref;
             }
+        }
+        f16x8 pb[kNR];
+#pragma unroll
+        for (int j = 0; j < kNR; ++j) {
             const float nm = -run_max[j];
             float pr[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], qk_row[j], nm));
+            for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j][i], qk_row[j], nm));
             pb[j] = f16x8{(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3],
                           (_Float16)pr[4], (_Float16)pr[5], (_Float16)pr[6], (_Float16)pr[7]};
             lsum[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[j], lsum[j], 0, 0, 0);
