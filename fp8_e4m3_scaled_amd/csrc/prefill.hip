@@ -19,7 +19,7 @@
 //   * online softmax per row in the log2 domain with the same lazy reference
 //     as the decode, P = exp2(fma(s, |qk|, -max)) from the raw MFMA scores;
 //     causal masking only on steps that reach the tile's first query
-//     position; the row sums come from one more MFMA with an all-ones V.
+//     position.
 // The next step's tiles are loaded into registers while the current one is
 // computed, then written to the other LDS buffer.
 
@@ -121,8 +121,13 @@ __device__ __forceinline__ const uint8_t *chunk_src(int c, const uint8_t *k_pool
     return v_pool + base + (int64_t)(tb / 4) * D * 4 + off;
 }
 
+// Three waves per SIMD for head dims up to 128 (a budget of 168 VGPRs).
+template <int D>
+struct Occupancy { static constexpr int WAVES = D <= 128 ? 3 : 1; };
+
 template <int D, int BS>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<D>::WAVES)))
+void prefill_kernel(PrefillArgs a) {
     constexpr int NC = D >= 128 ? D / 128 : 1;   // 128-dim K chunks per tile (D = 64: one, zero-padded)
     constexpr int MT = D / 16;
     constexpr int Q4 = D / 4;
@@ -253,21 +258,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 
     // run_max starts at a finite sentinel far below any score, so that
     // exp2(s*qk - run_max) of a masked score (-inf) is 0 without a select and
-    // the first rescale factor exp2(sentinel - ref) is 0.  The row sums are
-    // accumulated by the MFMA with an all-ones A operand (sum_k P[row][k] in
-    // every output dim), from the same f16 P as the numerator.
+    // the first rescale factor exp2(sentinel - ref) is 0.  run_sum holds this
+    // lane's share of the row sum (its four k-groups are added at the end).
     f32x4 acc[kNR][MT];
-    f32x4 lsum[kNR];
+    float run_sum[kNR];
     float run_max[kNR];
 #pragma unroll
     for (int j = 0; j < kNR; ++j) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        lsum[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        run_sum[j] = 0.0f;
         run_max[j] = kNoMax;
     }
-    const f16x8 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
-                        (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
 
     // Block ids come through the constant address space: the index is uniform,
     // so these are scalar loads (lgkmcnt), not vector loads that would make
@@ -310,61 +312,37 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         asm volatile("s_barrier" ::: "memory");
         issue(s + kStages - 1);
 
-        // ---- operands of this step from LDS (same lane mapping as the decode's loads)
-        uint32_t kw[2][NW], vw[2][NW];
+        const bool diag = p + kStep > first_row_pos;      // some key may be past some row
+        const bool tail = p + kStep > total;              // keys past the sequence's cache
+        // ---- S^T for both row tiles, one 16-key K tile at a time (its codes
+        // are read from LDS right before its MFMAs, as they are: the lane's
+        // D/4 codes of the key), then the row maxima, then one wave vote for
+        // the lazy rescale: straight-line code for both tiles between the
+        // vote's branches, so their latency chains can interleave.
+        f32x4 sc[kNR][2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const u32x4 *kp = reinterpret_cast<const u32x4 *>(&lds[buf][t * TILE + (g * 16 + m) * Q4]);
-            const u32x4 *vp = reinterpret_cast<const u32x4 *>(&lds[buf][(2 + t) * TILE + (g * D + (D / 16) * m) * 4]);
+            v8i ka[NC];
 #pragma unroll
-            for (int i = 0; i < NW / 4; ++i) {
-                const u32x4 kq = kp[i], vq = vp[i];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kw[t][4 * i + e] = kq[e];
-                    vw[t][4 * i + e] = vq[e];
-                }
+            for (int c = 0; c < NC; ++c) {
+                u32x4 k0 = kp[2 * c], k1 = u32x4{0u, 0u, 0u, 0u};
+                if (NW > 4) k1 = kp[2 * c + 1];
+                ka[c] = v8i{(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
+                            (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
             }
-        }
-        const bool diag = p + kStep > first_row_pos;      // some key may be past some row
-        const bool tail = p + kStep > total;              // keys past the sequence's cache
-        if (tail) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int valid = total - (p + 16 * t + 4 * g);
-                const uint32_t keep = valid >= 4 ? 0xFFFFFFFFu : valid <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * valid));
-#pragma unroll
-                for (int i = 0; i < NW; ++i) vw[t][i] &= keep;
-            }
-        }
-        // K operands: the lane's D/4 codes of each tile, as they are
-        v8i ka[2][NC];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int c = 0; c < NC; ++c)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int wi = 8 * c + i;
-                    ka[t][c][i] = wi < NW ? (int)kw[t][wi < NW ? wi : 0] : 0;
-                }
-        // ---- S^T for both row tiles, then their row maxima, then one wave
-        // vote for the lazy rescale: straight-line code for both tiles between
-        // the vote's branches, so their latency chains can interleave.
-        f32x4 sc[kNR][2];
-#pragma unroll
-        for (int j = 0; j < kNR; ++j)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int j = 0; j < kNR; ++j) {
                 sc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    sc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[t][c], qh[j][c], sc[j][t], 0, 0,
+                    sc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[c], qh[j][c], sc[j][t], 0, 0,
                                                                                 0, kUnitScale, 0, kUnitScale);
-                    sc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[t][c], ql[j][c], sc[j][t], 0, 0,
+                    sc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[c], ql[j][c], sc[j][t], 0, 0,
                                                                                 0, kUnitScale, 0, kUnitScale);
                 }
             }
+        }
         float x[kNR][8];                                   // raw scores, scaled inside exp2
         float mx[kNR];
         bool grow = false;
@@ -395,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             for (int j = 0; j < kNR; ++j) {
                 const float ref = fmaxf(run_max[j], mx[j]);
                 const float alpha = __builtin_amdgcn_exp2f(run_max[j] - ref);
-                lsum[j] *= alpha;
+                run_sum[j] *= alpha;
 #pragma unroll
                 for (int t = 0; t < MT; ++t) acc[j][t] *= alpha;
                 run_max[j] = ref;
@@ -410,9 +388,33 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j][i], qk_row[j], nm));
             pb[j] = f16x8{(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3],
                           (_Float16)pr[4], (_Float16)pr[5], (_Float16)pr[6], (_Float16)pr[7]};
-            lsum[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[j], lsum[j], 0, 0, 0);
+            float ps = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ps += pr[i];
+            run_sum[j] += ps;
         }
-        // ---- O^T += V^T P^T, V operands converted once for both row tiles
+        // ---- O^T += V^T P^T, V operands read now and converted once for
+        // both row tiles (lane (m, g) holds keys 4g..4g+3 of dims (D/16)m..)
+        uint32_t vw[2][NW];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const u32x4 *vp = reinterpret_cast<const u32x4 *>(&lds[buf][(2 + t) * TILE + (g * D + (D / 16) * m) * 4]);
+#pragma unroll
+            for (int i = 0; i < NW / 4; ++i) {
+                const u32x4 vq = vp[i];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vw[t][4 * i + e] = vq[e];
+            }
+        }
+        if (tail) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int valid = total - (p + 16 * t + 4 * g);
+                const uint32_t keep = valid >= 4 ? 0xFFFFFFFFu : valid <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * valid));
+#pragma unroll
+                for (int i = 0; i < NW; ++i) vw[t][i] &= keep;
+            }
+        }
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             const f16x2 e0 = codes_to_f16x2<false>(vw[0][t]), e1 = codes_to_f16x2<true>(vw[0][t]);
@@ -428,7 +430,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     // ---- normalize and write: lane (n, g) holds rows n of its tiles, dims (D/16)(4g+r)+t
 #pragma unroll
     for (int j = 0; j < kNR; ++j) {
-        const float l = lsum[j][0];          // every output dim of the ones product holds the row sum
+        float l = run_sum[j];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
         if (!row_live[j]) continue;
         const int r = (wave * kNR + j) * 16 + m;
         const int tok = i0 + r / G;
