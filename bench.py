@@ -15,7 +15,9 @@ rotated so that a decode never reads the copy the previous decode read (the
 Prints one JSON line.  `value` is the decode's achieved HBM bandwidth
 (algorithmic bytes / decode time); decode tokens/s and kv_store tokens/s are
 reported beside it.  `roofline` is for the decode kernel; `cpu_baseline` is
-the CPU oracle timed on a bounded sample of the same workload.
+the CPU oracle timed on a bounded sample of the same workload (all host cores,
+with the single-thread figure beside it); `stream_read_ceiling` is a plain
+streaming read of 2 GiB buffers, the achievable-bandwidth ceiling.
 """
 from __future__ import annotations
 
@@ -214,6 +216,8 @@ def run_llama8b(args):
         "wall_s_timed": round(wall, 3),
     }
 
+    result["stream_read_ceiling"] = _stream_ceiling(kv, stream)
+    result["decode"]["frac_of_stream_ceiling"] = round(decode_gbps / result["stream_read_ceiling"]["GBps"], 4)
     if args.cpu_seconds > 0:
         result["cpu_baseline"], result["parity_sample"] = _cpu_baseline(
             w, K, V, slots, q, out, ks, vs, args.cpu_seconds)
@@ -222,13 +226,60 @@ def run_llama8b(args):
     return result
 
 
+def _stream_ceiling(kv, stream, nbytes=2 << 30, launches=20):
+    """A plain streaming read (kvf8_read_probe) of two alternating 2 GiB buffers:
+    the achievable read bandwidth of this part, reported beside the 8 TB/s figure."""
+    import torch
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    n_out = 1024
+    sink = torch.empty(n_out, dtype=torch.int32, device="cuda")
+    ms = _timed(lambda i: kv.kvf8_read_probe(bufs[i % 2], nbytes, sink, n_out, stream), launches, 3, stream)
+    gbps = nbytes / (float(np.median(ms)) * 1e-3) / 1e9
+    del bufs
+    return {"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes": nbytes,
+            "launches": launches, "kernel": "kvf8_read_probe (XOR-reduce read, 1024 workgroups)"}
+
+
+def _host_threads():
+    """Host cores this process may use (at most 16: the share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _timed_oracle(items, fn, budget_s):
+    """The oracle as it stands, timed twice on the same kind of work: one thread
+    until half the budget is used, then all host cores (a thread pool: the C
+    oracle releases the GIL) on the next items.  Returns the per-item results,
+    the two (items, seconds) pairs and the thread count."""
+    from concurrent.futures import ThreadPoolExecutor
+    results, single_t, i = [], 0.0, 0
+    while i < len(items) and single_t < budget_s / 2:
+        t0 = time.perf_counter()
+        results.append(fn(items[i]))
+        single_t += time.perf_counter() - t0
+        i += 1
+    single_n = i
+    n = _host_threads()
+    per_thread = max(1, single_n)
+    batch = items[i:i + n * per_thread]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        results += list(ex.map(fn, batch))
+    multi_t = time.perf_counter() - t0
+    return results, (single_n, single_t), (len(batch), multi_t), n
+
+
 def _cpu_baseline(w, K, V, slots, q, out, ks, vs, budget_s):
     """The CPU oracle on a bounded sample: (sequence, kv-head) groups in a seeded
-    order, all query heads of each group, until the time budget is used.  Also
-    compares the GPU decode output on those heads with the oracle (the same
-    tolerance as the tests)."""
+    order, all query heads of each group, one thread and then all host cores.
+    Also compares the GPU decode output on those heads with the oracle (the
+    same tolerance as the tests)."""
     import oracle
     from synth import bf16_bits
+    oracle._load()
     q_bits = bf16_bits(q)
     got = out.float().cpu().numpy()
     G = w.Hq // w.Hkv
@@ -238,35 +289,41 @@ def _cpu_baseline(w, K, V, slots, q, out, ks, vs, budget_s):
     kp = np.zeros((w.NB, w.Hkv, w.BS * w.D), np.uint8)
     vp = np.zeros_like(kp)
     offs = np.concatenate([[0], np.cumsum(w.total_lengths)])
-    stored = set()
-    done, elapsed, worst, bad, nbytes = 0, 0.0, 0.0, 0, 0
-    for b, kvh in order:
+    lens = w.total_lengths.astype(np.int32)
+    # the oracle reads only bytes it stored itself; stores are outside the timed calls
+    n_max = len(order)
+    for b in sorted({b for b, _ in order[:n_max]}):
         lo, hi = int(offs[b]), int(offs[b + 1])
-        if b not in stored:
-            kb = bf16_bits(K[lo:hi]).reshape(hi - lo, row)
-            vb = bf16_bits(V[lo:hi]).reshape(hi - lo, row)
-            oracle.store(kb, vb, slots[lo:hi], kp, vp, Hkv=w.Hkv, D=w.D, BS=w.BS, k_scale=ks, v_scale=vs)
-            stored.add(b)
+        oracle.store(bf16_bits(K[lo:hi]).reshape(hi - lo, row), bf16_bits(V[lo:hi]).reshape(hi - lo, row),
+                     slots[lo:hi], kp, vp, Hkv=w.Hkv, D=w.D, BS=w.BS, k_scale=ks, v_scale=vs)
+
+    def group(item):
+        b, kvh = item
         sel = np.array([[b, kvh * G + j] for j in range(G)], np.int32)
-        t0 = time.perf_counter()
-        ref = oracle.decode_attn(q_bits, kp, vp, w.block_tables, w.total_lengths.astype(np.int32),
-                                 Hq=w.Hq, Hkv=w.Hkv, D=w.D, BS=w.BS, k_scale=ks, v_scale=vs,
-                                 sm_scale=w.sm_scale(), sel=sel)
-        elapsed += time.perf_counter() - t0
-        for _, hh in sel:
-            err = np.abs(got[b, hh] - ref[b, hh])
-            worst = max(worst, float(err.max()))
-            bad += int((err > 2e-3 + 1e-2 * np.abs(ref[b, hh])).sum())
-        L = int(w.total_lengths[b])
-        nbytes += L * 2 * w.D + G * w.D * (2 + 2) + 4 * (-(-L // w.BS)) + 4
-        done += 1
-        if elapsed >= budget_s:
-            break
-    cpu = {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-           "sample": f"{done} of {w.B * w.Hkv} (sequence, kv-head) groups x {G} query heads, fp64 "
-                     f"single-threaded C oracle, {elapsed:.1f} s",
-           "tokens_per_s": round(done * G / w.Hq / elapsed, 4)}
-    parity = {"heads_checked": done * G, "max_abs_err_bf16_out": worst, "outside_tolerance": bad}
+        ref = oracle.decode_attn(q_bits, kp, vp, w.block_tables, lens, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
+                                 BS=w.BS, k_scale=ks, v_scale=vs, sm_scale=w.sm_scale(), sel=sel)
+        return item, ref[b, kvh * G:(kvh + 1) * G]
+
+    def nbytes(item):
+        L = int(w.total_lengths[item[0]])
+        return L * 2 * w.D + G * w.D * (2 + 2) + 4 * (-(-L // w.BS)) + 4
+
+    results, (n1, t1), (n2, t2), threads = _timed_oracle(order, group, budget_s)
+    worst, bad = 0.0, 0
+    for (b, kvh), ref in results:
+        g = got[b, kvh * G:(kvh + 1) * G]
+        err = np.abs(g - ref)
+        worst = max(worst, float(err.max()))
+        bad += int((err > 2e-3 + 1e-2 * np.abs(ref)).sum())
+    b1 = sum(nbytes(it) for it, _ in results[:n1])
+    b2 = sum(nbytes(it) for it, _ in results[n1:])
+    cpu = {"value": round(b2 / t2 / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n2} (sequence, kv-head) groups x {G} query heads on {threads} threads, fp64 C "
+                     f"oracle, {t2:.1f} s wall (seeded order over all {w.B * w.Hkv} groups)",
+           "single_thread": {"value": round(b1 / t1 / 1e9, 4), "cores": 1,
+                             "sample": f"{n1} groups, {t1:.1f} s"},
+           "tokens_per_s": round(n2 * G / w.Hq / t2, 4)}
+    parity = {"heads_checked": len(results) * G, "max_abs_err_bf16_out": worst, "outside_tolerance": bad}
     return cpu, parity
 
 
@@ -383,43 +440,51 @@ def run_prefill(args):
 
 
 def _cpu_prefill(w, q, out, ctx, n, budget_s):
-    """Oracle FLOP/s on sampled query rows (and their parity with the GPU output)."""
+    """Oracle FLOP/s on sampled query rows, one thread and then all host cores
+    (and the rows' parity with the GPU output)."""
     import oracle
     from synth import bf16_bits
+    oracle._load()
     # the oracle reads bytes that it stored itself: store every sequence again on the CPU
     okp = np.zeros((w.NB, w.Hkv, w.BS * w.D), np.uint8)
     ovp = np.zeros_like(okp)
     row = w.Hkv * w.D
+    ks, vs, _ = w.scales()
     for b in range(w.B):
         L = int(w.total_lengths[b])
         for lo in range(0, L, 8192):
             m = min(8192, L - lo)
             k, v = w.kv(b, lo, m, device=q.device)
             oracle.store(bf16_bits(k).reshape(m, row), bf16_bits(v).reshape(m, row), w.slots(b, lo, m),
-                         okp, ovp, Hkv=w.Hkv, D=w.D, BS=w.BS, k_scale=w.scales()[0], v_scale=w.scales()[1])
+                         okp, ovp, Hkv=w.Hkv, D=w.D, BS=w.BS, k_scale=ks, v_scale=vs)
     qb = bf16_bits(q)
     got = out.float().cpu().numpy()
     cu = (np.arange(w.B + 1) * n).astype(np.int32)
     rng = np.random.default_rng(11)
-    done, flops, elapsed, bad = 0, 0, 0.0, 0
-    ks, vs, _ = w.scales()
-    while elapsed < budget_s and done < 4096:
-        r = int(rng.integers(0, w.B * n))
-        hh = int(rng.integers(0, w.Hq))
-        t0 = time.perf_counter()
+    items = [(int(rng.integers(0, w.B * n)), int(rng.integers(0, w.Hq))) for _ in range(8192)]
+
+    def one(item):
+        r, hh = item
         ref = oracle.prefill_attn(qb, okp, ovp, cu, ctx, w.block_tables, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
                                   BS=w.BS, k_scale=ks, v_scale=vs, sm_scale=w.sm_scale(),
                                   sel=np.array([[r, hh]], np.int64))
-        elapsed += time.perf_counter() - t0
-        b = r // n
-        keys = int(ctx[b]) + (r - b * n) + 1
-        flops += 4 * w.D * keys
-        err = np.abs(got[r, hh] - ref[r, hh])
-        bad += int((err > 2e-3 + 1e-2 * np.abs(ref[r, hh])).sum())
-        done += 1
-    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} random (query row, head) pairs, fp64 single-threaded C oracle "
-                      f"(including the per-row dequantizing gather), {elapsed:.1f} s",
+        return item, ref[r, hh]
+
+    def flops(item):
+        b = item[0] // n
+        return 4 * w.D * (int(ctx[b]) + (item[0] - b * n) + 1)
+
+    results, (n1, t1), (n2, t2), threads = _timed_oracle(items, one, budget_s)
+    bad = 0
+    for (r, hh), ref in results:
+        err = np.abs(got[r, hh] - ref)
+        bad += int((err > 2e-3 + 1e-2 * np.abs(ref)).sum())
+    f1 = sum(flops(it) for it, _ in results[:n1])
+    f2 = sum(flops(it) for it, _ in results[n1:])
+    return {"value": round(f2 / t2 / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n2} random (query row, head) pairs on {threads} threads, fp64 C oracle "
+                      f"(including the per-row dequantizing gather), {t2:.1f} s wall",
+            "single_thread": {"value": round(f1 / t1 / 1e12, 6), "cores": 1, "sample": f"{n1} rows, {t1:.1f} s"},
             "parity_outside_tolerance": bad}
 
 

@@ -43,6 +43,7 @@ SIGNATURES = {
     "paged_attn_prefill_chunk": (I32, [P, I32, P, I32, P, P, P, I32, I32, I64, I32, I32, F32, P,
                                        I32, P]),
     "kv_shift_rope": (I32, [P, I32, P, I64, I32, F32, I32, I32, P]),
+    "kvf8_read_probe": (I32, [P, SZ, P, I32, P]),
 }
 
 
@@ -214,3 +215,7 @@ def kv_shift_rope(cache, layer: int, slots, n_slots: int, delta: int, theta_base
                   rot_dim: int, style: int, stream=None) -> None:
     _check(_lib.kv_shift_rope(cache, layer, _ptr(slots), n_slots, delta, theta_base, rot_dim, style,
                               _stream(stream)))
+
+
+def kvf8_read_probe(buf, nbytes: int, out_words, n_out: int, stream=None) -> None:
+    _check(_lib.kvf8_read_probe(_ptr(buf), nbytes, _ptr(out_words), n_out, _stream(stream)))

@@ -499,4 +499,15 @@ kvf8_status kv_shift_rope(kvf8_cache *c, int32_t layer, const int64_t *slots, in
     return ok();
 }
 
+kvf8_status kvf8_read_probe(const void *buf, size_t bytes, uint32_t *out_words, int32_t n_out, void *stream) {
+    if (bytes == 0) return ok();
+    if (!buf || !out_words) return fail(KVF8_E_INVALID, "buf and out_words must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(buf) % 16) != 0 || bytes % 16 != 0)
+        return fail(KVF8_E_INVALID, "buf must be 16-byte aligned and bytes a multiple of 16");
+    if (n_out < 1 || n_out > (1 << 20)) return fail(KVF8_E_INVALID, "n_out must be in [1, 2^20]");
+    hipError_t e = kvf8::launch_read_probe(buf, (int64_t)bytes, out_words, n_out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kvf8_read_probe launch");
+    return ok();
+}
+
 }  // extern "C"

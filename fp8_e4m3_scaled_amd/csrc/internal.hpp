@@ -114,4 +114,7 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
+// ---------------------------------------------------------------- read probe
+hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int32_t n_out, hipStream_t stream);
+
 }  // namespace kvf8

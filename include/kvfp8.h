@@ -267,6 +267,18 @@ kvf8_status kv_shift_rope(kvf8_cache *cache, int32_t layer, const int64_t *slots
                           int64_t n_slots, int32_t delta, float theta_base, int32_t rot_dim,
                           kvf8_rope style, void *stream);
 
+/*
+ * Measurement aid, not a step of the cache: a plain streaming read of `bytes`
+ * of device memory at `buf` (16-byte aligned, bytes a multiple of 16), the
+ * achievable read-bandwidth ceiling that the cache kernels are reported
+ * beside.  n_out workgroups (1 <= n_out <= 2^20) read the buffer grid-stride;
+ * workgroup i writes the XOR of every 32-bit word it read to out_words[i]
+ * (device, n_out words, caller-owned), so the XOR of all out_words equals the
+ * XOR of the buffer's 32-bit words.  Asynchronous on `stream`.
+ */
+kvf8_status kvf8_read_probe(const void *buf, size_t bytes, uint32_t *out_words, int32_t n_out,
+                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -245,3 +245,17 @@ def test_one_hip_runtime_per_process(order):
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr[-2000:]
     assert out.stdout.startswith("1 "), out.stdout
+
+
+def test_read_probe_host_checks():
+    """The measurement read refuses misaligned or ragged buffers and bad worker counts
+    before launching anything; zero bytes is a no-op."""
+    kv.kvf8_read_probe(None, 0, None, 1, 0)
+    for buf, nbytes, n_out in [((1 << 30) + 4, 64, 8), (1 << 30, 60, 8), (1 << 30, 64, 0),
+                               (1 << 30, 64, (1 << 20) + 1)]:
+        with pytest.raises(kv.KvF8Error) as ei:
+            kv.kvf8_read_probe(buf, nbytes, 1 << 30, n_out, 0)
+        assert ei.value.status == kv.E_INVALID
+    with pytest.raises(kv.KvF8Error) as ei:
+        kv.kvf8_read_probe(1 << 30, 64, None, 8, 0)
+    assert ei.value.status == kv.E_INVALID
