@@ -2,14 +2,21 @@
 
 Every workload is stored and computed on the GPU exactly as the benchmark does
 it (the same store calls, one decode / prefill launch over the whole batch,
-the same split plan, bf16 outputs).  The oracle then checks a seeded sample
-it can afford: for each sampled sequence it stores that sequence's own bf16
-K/V into compact pools (the sampled sequences only, blocks renumbered), and
-  * the GPU bytes of the sequence's blocks must equal the oracle's bit for bit;
-  * the sampled attention outputs must satisfy |gpu - oracle| <= 2e-3 + 1e-2|oracle|.
-Inputs come from the seeded generators on the GPU and are handed to both
-sides as the same bf16 bits; no expected value comes from the HIP library.
+the same split plan, bf16 outputs).  The oracle stores every sequence's own
+bf16 K/V into full-size host pools with the same block tables (inputs come
+from the seeded generators on the GPU and reach both sides as the same bf16
+bits; no expected value comes from the HIP library), and
+  * the whole K and V pools must equal the oracle's bit for bit;
+  * attention outputs satisfy |gpu - oracle| <= 2e-3 + 1e-2 |oracle|:
+    every (sequence, head) of the Llama-shaped and variable-length decodes and
+    of both long-context decodes, and 8,192 prefill (query, head) rows that
+    include the first and last 32 query tokens of every sequence (all heads).
+Oracle calls run on a thread pool over disjoint sequences / groups (the C
+oracle keeps no shared state and releases the GIL).
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -23,6 +30,20 @@ from tests.test_gpu_decode import assert_close
 pytestmark = pytest.mark.gpu
 
 FILL_STEP = 65536
+
+
+def _threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _pmap(fn, items):
+    oracle._load()
+    with ThreadPoolExecutor(max_workers=_threads()) as ex:
+        return list(ex.map(fn, items))
 
 
 class FullCache:
@@ -49,11 +70,9 @@ class FullCache:
                                 t_dev(w.slots(b, lo, n)), n)
         torch.cuda.synchronize()
 
-    def blocks(self, b, L):
-        """GPU bytes of the blocks that hold tokens 0..L-1 of sequence b."""
-        idx = torch.from_numpy(self.w.block_tables[b, :-(-L // self.w.BS)].astype(np.int64)).to(DEV)
+    def pools(self):
         torch.cuda.synchronize()
-        return self.k_pool[idx].cpu().numpy(), self.v_pool[idx].cpu().numpy()
+        return self.k_pool.cpu().numpy(), self.v_pool.cpu().numpy()
 
     def close(self):
         if self.handle:
@@ -61,51 +80,45 @@ class FullCache:
             self.handle = None
 
 
-class OracleSample:
-    """Oracle pools holding only the sampled sequences, blocks renumbered."""
+class OraclePools:
+    """Full-size oracle pools: every sequence's tokens [lo, hi) stored by the oracle."""
 
-    def __init__(self, w: Workload, seqs, lens, ks, vs):
-        self.w, self.seqs = w, list(seqs)
-        self.lens = np.array([int(lens[b]) for b in self.seqs], np.int64)
-        nblk = [-(-int(L) // w.BS) for L in self.lens]
-        self.table = np.zeros((len(self.seqs), max(nblk)), np.int32)
-        off = 0
-        for i, n in enumerate(nblk):
-            self.table[i, :n] = np.arange(off, off + n)
-            off += n
-        self.nblk = nblk
-        self.kp = np.zeros((off, w.Hkv, w.BS * w.D), np.uint8)
+    def __init__(self, w: Workload, ks, vs):
+        self.w, self.ks, self.vs = w, ks, vs
+        self.kp = np.zeros((w.NB, w.Hkv, w.BS * w.D), np.uint8)
         self.vp = np.zeros_like(self.kp)
-        self.ks, self.vs = ks, vs
-        for i, b in enumerate(self.seqs):
-            self.store(i, 0, int(self.lens[i]))
 
-    def slots(self, i, lo, n):
-        p = np.arange(lo, lo + n, dtype=np.int64)
-        return self.table[i, p // self.w.BS].astype(np.int64) * self.w.BS + p % self.w.BS
-
-    def store(self, i, lo, count):
-        w, b = self.w, self.seqs[i]
-        for s in range(lo, lo + count, FILL_STEP):
-            n = min(FILL_STEP, lo + count - s)
-            k, v = w.kv(b, s, n, device=DEV)
-            oracle.store(bf16_bits(k), bf16_bits(v), self.slots(i, s, n), self.kp, self.vp,
-                         Hkv=w.Hkv, D=w.D, BS=w.BS, k_scale=self.ks, v_scale=self.vs)
-
-    def check_bytes(self, cache: FullCache):
-        for i, b in enumerate(self.seqs):
-            gk, gv = cache.blocks(b, int(self.lens[i]))
-            rows = self.table[i, :self.nblk[i]]
-            assert np.array_equal(gk, self.kp[rows]), f"K bytes of sequence {b} differ"
-            assert np.array_equal(gv, self.vp[rows]), f"V bytes of sequence {b} differ"
-
-    def decode(self, q_bits, heads):
-        """Oracle decode of the sampled sequences; returns [len(seqs)][Hq][D] (NaN off `heads`)."""
+    def store(self, ranges):
+        """ranges: (b, lo, hi) triples; different sequences write disjoint slots."""
         w = self.w
-        sel = np.array([[i, h] for i in range(len(self.seqs)) for h in heads], np.int32)
-        return oracle.decode_attn(q_bits[self.seqs], self.kp, self.vp, self.table,
-                                  self.lens.astype(np.int32), Hq=w.Hq, Hkv=w.Hkv, D=w.D, BS=w.BS,
-                                  k_scale=self.ks, v_scale=self.vs, sm_scale=w.sm_scale(), sel=sel)
+
+        def one(r):
+            b, lo, hi = r
+            for s in range(lo, hi, FILL_STEP):
+                n = min(FILL_STEP, hi - s)
+                k, v = w.kv(b, s, n, device=DEV)
+                oracle.store(bf16_bits(k), bf16_bits(v), w.slots(b, s, n), self.kp, self.vp,
+                             Hkv=w.Hkv, D=w.D, BS=w.BS, k_scale=self.ks, v_scale=self.vs)
+        _pmap(one, ranges)
+
+    def check_bytes(self, cache: FullCache, what):
+        gk, gv = cache.pools()
+        nk = int(np.count_nonzero(gk != self.kp))
+        nv = int(np.count_nonzero(gv != self.vp))
+        assert nk == 0 and nv == 0, f"{what}: {nk} K and {nv} V bytes differ from the oracle"
+
+    def decode_all(self, q_bits, lens):
+        """Oracle decode of every (sequence, head): [B][Hq][D] fp64."""
+        w = self.w
+        lens = np.asarray(lens, np.int32)
+
+        def one(b):
+            sel = np.array([[b, h] for h in range(w.Hq)], np.int32)
+            ref = oracle.decode_attn(q_bits, self.kp, self.vp, w.block_tables, lens, Hq=w.Hq, Hkv=w.Hkv,
+                                     D=w.D, BS=w.BS, k_scale=self.ks, v_scale=self.vs,
+                                     sm_scale=w.sm_scale(), sel=sel)
+            return ref[b]
+        return np.stack(_pmap(one, range(w.B)))
 
 
 def _decode_full(w, cache, q, lens):
@@ -121,16 +134,9 @@ def _decode_full(w, cache, q, lens):
     return out.float().cpu().numpy(), ws_bytes
 
 
-def _check_decode(w, sample, got, q, heads, what):
-    want = sample.decode(bf16_bits(q), heads)
-    for i, b in enumerate(sample.seqs):
-        assert_close(got[b][heads], want[i][heads], f"{what} sequence {b}")
-    assert np.isfinite(got).all(), f"{what}: non-finite outputs"
-
-
 def test_llama8b_full_size():
     """64 x 4096 tokens, 32 q / 8 kv heads, D 128, block 16: one store launch
-    over all 262,144 tokens, one decode launch; 4 sampled sequences, all heads."""
+    over all 262,144 tokens, one decode launch; all bytes, all 2,048 heads."""
     w = Workload("llama8b", device=DEV)
     cache = FullCache(w)
     try:
@@ -152,17 +158,18 @@ def test_llama8b_full_size():
         q = w.q_decode(DEV)
         got, ws_bytes = _decode_full(w, cache, q, w.total_lengths)
         assert ws_bytes == 0                       # the benchmark's plan: one chunk per sequence
-        seqs = np.random.default_rng(11).choice(w.B, 4, replace=False)
-        sample = OracleSample(w, seqs, w.total_lengths, cache.ks, cache.vs)
-        sample.check_bytes(cache)
-        _check_decode(w, sample, got, q, list(range(w.Hq)), "llama8b decode")
+        orc = OraclePools(w, cache.ks, cache.vs)
+        orc.store([(b, 0, int(w.total_lengths[b])) for b in range(w.B)])
+        orc.check_bytes(cache, "llama8b")
+        want = orc.decode_all(bf16_bits(q), w.total_lengths)
+        assert_close(got, want, "llama8b decode, every head")
     finally:
         cache.close()
 
 
 def test_varlen_full_size():
     """256 sequences with lengths in [512, 32768] (+1 new token), bf16 scales,
-    8 splits + reduce; the shortest, the longest and 3 seeded sequences."""
+    8 splits + reduce; all 8.7 GB of cache bytes and all 8,192 heads."""
     w = Workload("varlen", device=DEV, pool_frac=0.0)    # compact pool; same launch shapes
     cache = FullCache(w)
     try:
@@ -177,21 +184,20 @@ def test_varlen_full_size():
         q = w.q_decode(DEV)
         got, ws_bytes = _decode_full(w, cache, q, w.total_lengths)
         assert ws_bytes > 0                        # split-K with the reduce, as benchmarked
-        rng = np.random.default_rng(12)
-        seqs = sorted({int(np.argmin(w.total_lengths)), int(np.argmax(w.total_lengths)),
-                       *rng.choice(w.B, 3, replace=False).tolist()})
-        sample = OracleSample(w, seqs, w.total_lengths, cache.ks, cache.vs)
-        sample.check_bytes(cache)
-        heads = sorted(rng.choice(w.Hq, 8, replace=False).tolist())
-        _check_decode(w, sample, got, q, heads, "varlen decode")
+        orc = OraclePools(w, cache.ks, cache.vs)
+        orc.store([(b, 0, int(w.total_lengths[b])) for b in range(w.B)])
+        orc.check_bytes(cache, "varlen")
+        want = orc.decode_all(bf16_bits(q), w.total_lengths)
+        assert_close(got, want, "varlen decode, every head")
     finally:
         cache.close()
 
 
 def test_longctx_full_size_with_shift():
     """8 x 131072 tokens, 16 q / 2 kv heads, D 256, block 32, 32 splits: decode,
-    K-shift of every cached token by -4096 (theta 1e6, NEOX), decode again;
-    one sampled sequence through the oracle's own chain."""
+    K-shift of every cached token by -4096 (theta 1e6, NEOX), decode again; all
+    bytes after the shift and every head of both decodes against the oracle's
+    own chain."""
     w = Workload("longctx", device=DEV)
     cache = FullCache(w)
     try:
@@ -199,29 +205,31 @@ def test_longctx_full_size_with_shift():
         cache.fill(w.lengths)
         lens = w.lengths
         q = w.q_decode(DEV)
+        qb = bf16_bits(q)
         got1, ws_bytes = _decode_full(w, cache, q, lens)
         assert ws_bytes > 0
         slots = np.concatenate([w.slots(b, 0, int(lens[b])) for b in range(w.B)])
         kv.kv_shift_rope(cache.handle, 0, t_dev(slots), slots.size, w.spec.delta, w.spec.theta, w.D,
                          kv.ROPE_NEOX)
         got2, _ = _decode_full(w, cache, q, lens)
-        seqs = [int(np.random.default_rng(13).integers(w.B))]
-        sample = OracleSample(w, seqs, lens, cache.ks, cache.vs)
-        heads = list(range(w.Hq))
-        _check_decode(w, sample, got1, q, heads, "longctx decode before shift")
-        osl = np.concatenate([sample.slots(i, 0, int(sample.lens[i])) for i in range(len(seqs))])
-        oracle.kshift(sample.kp, osl, Hkv=w.Hkv, D=w.D, BS=w.BS, delta=w.spec.delta,
-                      theta=w.spec.theta, rot_dim=w.D, neox=True)
-        sample.check_bytes(cache)
-        _check_decode(w, sample, got2, q, heads, "longctx decode after shift")
+        orc = OraclePools(w, cache.ks, cache.vs)
+        orc.store([(b, 0, int(lens[b])) for b in range(w.B)])
+        assert_close(got1, orc.decode_all(qb, lens), "longctx decode before shift, every head")
+        # the oracle's own shift, per sequence (disjoint slots)
+        _pmap(lambda b: oracle.kshift(orc.kp, w.slots(b, 0, int(lens[b])), Hkv=w.Hkv, D=w.D, BS=w.BS,
+                                      delta=w.spec.delta, theta=w.spec.theta, rot_dim=w.D, neox=True),
+              range(w.B))
+        orc.check_bytes(cache, "longctx after shift")
+        assert_close(got2, orc.decode_all(qb, lens), "longctx decode after shift, every head")
     finally:
         cache.close()
 
 
 def test_prefill_full_size():
     """4 sequences x (16384 cached + 2048-token chunk), 32 q / 8 kv heads: the
-    chunk's store launch then one prefill launch; 48 sampled (query, head) rows
-    that include each chunk's first and last token."""
+    chunk's store launch then one prefill launch; all bytes, and 8,192 (query,
+    head) rows: the first and last 32 tokens of every chunk with all heads,
+    plus seeded rows in between."""
     w = Workload("prefill", device=DEV)
     cache = FullCache(w)
     try:
@@ -244,18 +252,30 @@ def test_prefill_full_size():
         torch.cuda.synchronize()
         got = out.float().cpu().numpy()
         assert np.isfinite(got).all()
-        seqs = list(range(w.B))
-        sample = OracleSample(w, seqs, w.total_lengths, cache.ks, cache.vs)
-        sample.check_bytes(cache)
+        orc = OraclePools(w, cache.ks, cache.vs)
+        orc.store([(b, 0, int(w.total_lengths[b])) for b in range(w.B)])
+        orc.check_bytes(cache, "prefill")
         rng = np.random.default_rng(14)
-        rows = [(b * n, int(rng.integers(w.Hq))) for b in range(w.B)]
-        rows += [(b * n + n - 1, int(rng.integers(w.Hq))) for b in range(w.B)]
-        rows += [(int(rng.integers(T)), int(rng.integers(w.Hq))) for _ in range(40)]
-        sel = np.array(rows, np.int64)
-        want = oracle.prefill_attn(bf16_bits(q), sample.kp, sample.vp, cu, ctx, sample.table, Hq=w.Hq,
-                                   Hkv=w.Hkv, D=w.D, BS=w.BS, k_scale=cache.ks, v_scale=cache.vs,
-                                   sm_scale=w.sm_scale(), sel=sel)
-        for qi, h in rows:
-            assert_close(got[qi, h], want[qi, h], f"prefill row {qi} head {h}")
+        rows = set()
+        for b in range(w.B):
+            for i in list(range(32)) + list(range(n - 32, n)):
+                rows.update((b * n + i, h) for h in range(w.Hq))
+        while len(rows) < 8192:
+            rows.add((int(rng.integers(T)), int(rng.integers(w.Hq))))
+        G = w.Hq // w.Hkv
+        groups = {}
+        for qi, h in sorted(rows):
+            groups.setdefault((qi // n, h // G), []).append((qi, h))
+        qb = bf16_bits(q)
+
+        def one(key):
+            sel = np.array(sorted(groups[key]), np.int64)
+            ref = oracle.prefill_attn(qb, orc.kp, orc.vp, cu, ctx, w.block_tables, Hq=w.Hq, Hkv=w.Hkv,
+                                      D=w.D, BS=w.BS, k_scale=cache.ks, v_scale=cache.vs,
+                                      sm_scale=w.sm_scale(), sel=sel)
+            return sel, ref[sel[:, 0], sel[:, 1]]
+        for sel, ref in _pmap(one, sorted(groups)):
+            assert_close(got[sel[:, 0], sel[:, 1]], ref, f"prefill rows of group ({sel[0, 0] // n}, ...)")
+        assert len(rows) >= 4096
     finally:
         cache.close()
