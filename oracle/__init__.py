@@ -74,6 +74,13 @@ def _load():
         "orc_decode_attn": (ctypes.c_int, [P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, P, ctypes.c_int, P, ctypes.c_int,
                                            f32, f32, f64, P, i64, P]),
+        "orc_store_typed": (None, [P, P, i64, i64, P, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   i64, ctypes.c_int, ctypes.c_int, f32, f32, P, P]),
+        "orc_gather_typed": (None, [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, P, ctypes.c_int, ctypes.c_int, f32, f32, P, P]),
+        "orc_decode_attn_typed": (ctypes.c_int, [P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int,
+                                                 P, ctypes.c_int, f32, f32, f64, P, i64, P]),
         "orc_prefill_attn": (ctypes.c_int, [P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int, P, P, P, ctypes.c_int, ctypes.c_int,
                                             f32, f32, f64, P, i64, P]),
@@ -142,34 +149,41 @@ def kv_bytes_per_block(BS: int, Hkv: int, D: int, elem_bytes: int) -> int:
 
 
 # ---------------------------------------------------------------- store
+def _elem_bytes(pool) -> int:
+    """Element bytes of an oracle pool: uint8 holds E4M3 codes, uint16 bf16 values."""
+    assert pool.dtype in (np.uint8, np.uint16) and pool.flags.c_contiguous
+    return pool.dtype.itemsize
+
+
 def store(k_bits, v_bits, slots, k_pool, v_pool, *, Hkv: int, D: int, BS: int,
           k_scale: float, v_scale: float) -> None:
-    """Quantize bf16 K/V rows [T][Hkv][D] into the byte pools in place.
+    """Store bf16 K/V rows [T][Hkv][D] into the pools in place.
 
-    k_pool / v_pool: uint8 arrays [NB][Hkv][BS*D] (modified in place).  Slots
-    that are negative or at or past NB*BS are skipped."""
+    k_pool / v_pool: [NB][Hkv][BS*D] arrays, uint8 for an E4M3 pool (values
+    quantized) or uint16 for a bf16 pool (the bf16 bits as given; its scale
+    must be 1).  Slots that are negative or at or past NB*BS are skipped."""
     k = _c(k_bits, np.uint16).reshape(-1, Hkv * D)
     v = _c(v_bits, np.uint16).reshape(-1, Hkv * D)
     s = _c(slots, np.int64)
     assert k.shape[0] == v.shape[0] == s.shape[0]
-    assert k_pool.dtype == np.uint8 and v_pool.dtype == np.uint8
-    assert k_pool.flags.c_contiguous and v_pool.flags.c_contiguous
+    keb, veb = _elem_bytes(k_pool), _elem_bytes(v_pool)
     assert k_pool.size == v_pool.size and k_pool.size % (Hkv * BS * D) == 0
     NB = k_pool.size // (Hkv * BS * D)
-    _load().orc_store(_ptr(k), _ptr(v), Hkv * D, Hkv * D, _ptr(s), s.size, Hkv, D, BS, NB,
-                      float(np.float32(k_scale)), float(np.float32(v_scale)),
-                      _ptr(k_pool), _ptr(v_pool))
+    _load().orc_store_typed(_ptr(k), _ptr(v), Hkv * D, Hkv * D, _ptr(s), s.size, Hkv, D, BS, NB, keb, veb,
+                            float(np.float32(k_scale)), float(np.float32(v_scale)),
+                            _ptr(k_pool), _ptr(v_pool))
 
 
 def gather_dequant(k_pool, v_pool, table, L: int, h: int, *, Hkv: int, D: int, BS: int,
                    k_scale: float, v_scale: float):
-    """Dequantized fp32 K and V rows [L][D] of one sequence / kv-head."""
+    """Dequantized fp32 K and V rows [L][D] of one sequence / kv-head (uint8 pools
+    hold E4M3 codes, uint16 pools bf16 values)."""
     t = _c(table, np.int32)
     kd = np.empty((L, D), np.float32)
     vd = np.empty((L, D), np.float32)
-    _load().orc_gather_dequant(_ptr(k_pool), _ptr(v_pool), Hkv, D, BS, _ptr(t), L, h,
-                               float(np.float32(k_scale)), float(np.float32(v_scale)),
-                               _ptr(kd), _ptr(vd))
+    _load().orc_gather_typed(_ptr(k_pool), _ptr(v_pool), Hkv, D, BS, _elem_bytes(k_pool), _elem_bytes(v_pool),
+                             _ptr(t), L, h, float(np.float32(k_scale)), float(np.float32(v_scale)),
+                             _ptr(kd), _ptr(vd))
     return kd, vd
 
 
@@ -178,6 +192,7 @@ def decode_attn(q_bits, k_pool, v_pool, block_tables, seq_lens, *, Hq: int, Hkv:
                 BS: int, k_scale: float, v_scale: float, sm_scale: float, sel=None) -> np.ndarray:
     """fp64 paged decode attention. q_bits [B][Hq][D] bf16 bits -> out [B][Hq][D] fp64.
 
+    k_pool / v_pool: uint8 (E4M3 codes) or uint16 (bf16 values) arrays.
     sel: optional int array [n][2] of (b, h) pairs; other outputs are NaN."""
     q = _c(q_bits, np.uint16)
     B = q.shape[0]
@@ -189,9 +204,10 @@ def decode_attn(q_bits, k_pool, v_pool, block_tables, seq_lens, *, Hq: int, Hkv:
         sp, n = _ptr(s), s.shape[0]
     else:
         s, sp, n = None, None, 0
-    rc = _load().orc_decode_attn(_ptr(q), Hq, _ptr(k_pool), _ptr(v_pool), Hkv, D, BS, _ptr(bt),
-                                 bt.shape[1], _ptr(sl), B, float(np.float32(k_scale)),
-                                 float(np.float32(v_scale)), float(sm_scale), sp, n, _ptr(out))
+    rc = _load().orc_decode_attn_typed(_ptr(q), Hq, _ptr(k_pool), _ptr(v_pool), Hkv, D, BS,
+                                       _elem_bytes(k_pool), _elem_bytes(v_pool), _ptr(bt),
+                                       bt.shape[1], _ptr(sl), B, float(np.float32(k_scale)),
+                                       float(np.float32(v_scale)), float(sm_scale), sp, n, _ptr(out))
     if rc != 0:
         raise MemoryError("oracle scratch allocation failed")
     return out
@@ -203,6 +219,7 @@ def prefill_attn(q_bits, k_pool, v_pool, cu_q_lens, context_lens, block_tables, 
     """fp64 causal chunked-prefill attention over the cache. q [total_q][Hq][D] -> fp64.
 
     sel: optional int array [n][2] of (global query index, head) pairs."""
+    assert k_pool.dtype == np.uint8 and v_pool.dtype == np.uint8, "the prefill oracle reads E4M3 pools"
     q = _c(q_bits, np.uint16)
     cu = _c(cu_q_lens, np.int32)
     cl = _c(context_lens, np.int32)

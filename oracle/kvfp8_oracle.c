@@ -179,11 +179,11 @@ static int64_t orc_tile_base(int64_t block, int h, int Hkv, int BS, int D)
 /* NB * BS slots, means "skip this token".                              */
 /* k, v: [T][Hkv][D] bf16 bits with a token stride in elements.         */
 /* ------------------------------------------------------------------ */
-void orc_store(const uint16_t *k, const uint16_t *v,
-               int64_t k_tok_stride, int64_t v_tok_stride,
-               const int64_t *slots, int64_t T,
-               int Hkv, int D, int BS, int64_t NB, float k_scale, float v_scale,
-               uint8_t *k_pool, uint8_t *v_pool)
+void orc_store_typed(const uint16_t *k, const uint16_t *v,
+                     int64_t k_tok_stride, int64_t v_tok_stride,
+                     const int64_t *slots, int64_t T,
+                     int Hkv, int D, int BS, int64_t NB, int k_eb, int v_eb,
+                     float k_scale, float v_scale, void *k_pool, void *v_pool)
 {
     const float k_inv = 1.0f / k_scale;
     const float v_inv = 1.0f / v_scale;
@@ -196,37 +196,75 @@ void orc_store(const uint16_t *k, const uint16_t *v,
         for (int h = 0; h < Hkv; ++h) {
             const int64_t base = orc_tile_base(block, h, Hkv, BS, D);
             for (int d = 0; d < D; ++d) {
-                const float xk = orc_bf16_to_f32(k[i * k_tok_stride + (int64_t)h * D + d]);
-                const float xv = orc_bf16_to_f32(v[i * v_tok_stride + (int64_t)h * D + d]);
-                const float yk = isnan(xk) ? xk : xk * k_inv;
-                const float yv = isnan(xv) ? xv : xv * v_inv;
-                k_pool[base + orc_k_tile_offset(t, d, BS, D)] = orc_e4m3_encode(yk);
-                v_pool[base + orc_v_tile_offset(t, d, BS, D)] = orc_e4m3_encode(yv);
+                const uint16_t bk = k[i * k_tok_stride + (int64_t)h * D + d];
+                const uint16_t bv = v[i * v_tok_stride + (int64_t)h * D + d];
+                const int64_t ek = base + orc_k_tile_offset(t, d, BS, D);
+                const int64_t ev = base + orc_v_tile_offset(t, d, BS, D);
+                if (k_eb == 2) {
+                    ((uint16_t *)k_pool)[ek] = bk;
+                } else {
+                    const float xk = orc_bf16_to_f32(bk);
+                    ((uint8_t *)k_pool)[ek] = orc_e4m3_encode(isnan(xk) ? xk : xk * k_inv);
+                }
+                if (v_eb == 2) {
+                    ((uint16_t *)v_pool)[ev] = bv;
+                } else {
+                    const float xv = orc_bf16_to_f32(bv);
+                    ((uint8_t *)v_pool)[ev] = orc_e4m3_encode(isnan(xv) ? xv : xv * v_inv);
+                }
             }
         }
     }
 }
 
+void orc_store(const uint16_t *k, const uint16_t *v,
+               int64_t k_tok_stride, int64_t v_tok_stride,
+               const int64_t *slots, int64_t T,
+               int Hkv, int D, int BS, int64_t NB, float k_scale, float v_scale,
+               uint8_t *k_pool, uint8_t *v_pool)
+{
+    orc_store_typed(k, v, k_tok_stride, v_tok_stride, slots, T, Hkv, D, BS, NB, 1, 1,
+                    k_scale, v_scale, k_pool, v_pool);
+}
+
 /* ------------------------------------------------------------------ */
 /* Gather the dequantized fp32 K and V rows of one sequence and one     */
 /* kv-head, in position order, following the block table:               */
-/* Kd = fl32(decode(code) * s_k), Vd = fl32(decode(code) * s_v).        */
+/* Kd = fl32(decode(code) * s_k), Vd = fl32(decode(code) * s_v).  A     */
+/* bf16 pool (element bytes 2) holds the values themselves: Kd = the    */
+/* bf16 value times its scale (1 for such a pool).                      */
 /* ------------------------------------------------------------------ */
-void orc_gather_dequant(const uint8_t *k_pool, const uint8_t *v_pool,
-                        int Hkv, int D, int BS,
-                        const int32_t *table, int L, int h,
-                        float k_scale, float v_scale,
-                        float *kd, float *vd)
+static float orc_element(const void *pool, int eb, int64_t e)
+{
+    if (eb == 2)
+        return orc_bf16_to_f32(((const uint16_t *)pool)[e]);
+    return orc_e4m3_decode(((const uint8_t *)pool)[e]);
+}
+
+void orc_gather_typed(const void *k_pool, const void *v_pool,
+                      int Hkv, int D, int BS, int k_eb, int v_eb,
+                      const int32_t *table, int L, int h,
+                      float k_scale, float v_scale,
+                      float *kd, float *vd)
 {
     for (int p = 0; p < L; ++p) {
         const int64_t block = table[p / BS];
         const int t = p % BS;
         const int64_t base = orc_tile_base(block, h, Hkv, BS, D);
         for (int d = 0; d < D; ++d) {
-            kd[(int64_t)p * D + d] = orc_e4m3_decode(k_pool[base + orc_k_tile_offset(t, d, BS, D)]) * k_scale;
-            vd[(int64_t)p * D + d] = orc_e4m3_decode(v_pool[base + orc_v_tile_offset(t, d, BS, D)]) * v_scale;
+            kd[(int64_t)p * D + d] = orc_element(k_pool, k_eb, base + orc_k_tile_offset(t, d, BS, D)) * k_scale;
+            vd[(int64_t)p * D + d] = orc_element(v_pool, v_eb, base + orc_v_tile_offset(t, d, BS, D)) * v_scale;
         }
     }
+}
+
+void orc_gather_dequant(const uint8_t *k_pool, const uint8_t *v_pool,
+                        int Hkv, int D, int BS,
+                        const int32_t *table, int L, int h,
+                        float k_scale, float v_scale,
+                        float *kd, float *vd)
+{
+    orc_gather_typed(k_pool, v_pool, Hkv, D, BS, 1, 1, table, L, h, k_scale, v_scale, kd, vd);
 }
 
 /* ------------------------------------------------------------------ */
@@ -271,13 +309,13 @@ static void orc_attend_row(const uint16_t *q, const float *kd, const float *vd,
 /* left untouched); NULL computes every (b, h).                         */
 /* Returns 0, or -1 when scratch memory cannot be allocated.            */
 /* ------------------------------------------------------------------ */
-int orc_decode_attn(const uint16_t *q, int Hq,
-                    const uint8_t *k_pool, const uint8_t *v_pool,
-                    int Hkv, int D, int BS,
-                    const int32_t *block_tables, int max_blocks,
-                    const int32_t *seq_lens, int B,
-                    float k_scale, float v_scale, double sm_scale,
-                    const int32_t *sel, int64_t n_sel, double *out)
+int orc_decode_attn_typed(const uint16_t *q, int Hq,
+                          const void *k_pool, const void *v_pool,
+                          int Hkv, int D, int BS, int k_eb, int v_eb,
+                          const int32_t *block_tables, int max_blocks,
+                          const int32_t *seq_lens, int B,
+                          float k_scale, float v_scale, double sm_scale,
+                          const int32_t *sel, int64_t n_sel, double *out)
 {
     const int g = Hq / Hkv;
     int maxL = 0;
@@ -297,13 +335,25 @@ int orc_decode_attn(const uint16_t *q, int Hq,
         const int h = sel ? sel[2 * i + 1] : (int)(i % Hq);
         const int L = seq_lens[b];
         const int kvh = h / g;
-        orc_gather_dequant(k_pool, v_pool, Hkv, D, BS, block_tables + (int64_t)b * max_blocks,
-                           L, kvh, k_scale, v_scale, kd, vd);
+        orc_gather_typed(k_pool, v_pool, Hkv, D, BS, k_eb, v_eb, block_tables + (int64_t)b * max_blocks,
+                         L, kvh, k_scale, v_scale, kd, vd);
         orc_attend_row(q + ((int64_t)b * Hq + h) * D, kd, vd, L, D, sm_scale, scores,
                        out + ((int64_t)b * Hq + h) * D);
     }
     free(kd); free(vd); free(scores);
     return 0;
+}
+
+int orc_decode_attn(const uint16_t *q, int Hq,
+                    const uint8_t *k_pool, const uint8_t *v_pool,
+                    int Hkv, int D, int BS,
+                    const int32_t *block_tables, int max_blocks,
+                    const int32_t *seq_lens, int B,
+                    float k_scale, float v_scale, double sm_scale,
+                    const int32_t *sel, int64_t n_sel, double *out)
+{
+    return orc_decode_attn_typed(q, Hq, k_pool, v_pool, Hkv, D, BS, 1, 1, block_tables, max_blocks,
+                                 seq_lens, B, k_scale, v_scale, sm_scale, sel, n_sel, out);
 }
 
 /* ------------------------------------------------------------------ */
