@@ -20,6 +20,7 @@ STATUS_NAMES = {0: "KVF8_OK", 1: "KVF8_E_INVALID", 2: "KVF8_E_SCALE", 3: "KVF8_E
                 4: "KVF8_E_NOBLOCKS", 5: "KVF8_E_UNSUPPORTED", 6: "KVF8_E_HIP"}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 ROPE_NORM, ROPE_NEOX = 0, 1
+ELEM_E4M3, ELEM_BF16 = 0, 1
 
 # (restype, argtypes) of every exported function, in header order
 P, I32, I64, U64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
@@ -29,6 +30,8 @@ SIGNATURES = {
     "kvf8_last_error": (ctypes.c_char_p, []),
     "kv_bytes_per_block": (SZ, [I32, I32, I32, I32]),
     "kv_cache_alloc": (I32, [I32, I64, I32, I32, I32, P, P, I32, P, P, ctypes.POINTER(P)]),
+    "kv_cache_alloc_typed": (I32, [I32, I64, I32, I32, I32, I32, I32, P, P, I32, P, P, ctypes.POINTER(P)]),
+    "kv_cache_elem_types": (I32, [P, P, P]),
     "kv_cache_free": (I32, [P]),
     "kv_cache_set_scales": (I32, [P, I32, P, P, I32]),
     "kv_cache_get_scales": (I32, [P, I32, P, P]),
@@ -135,6 +138,25 @@ def kv_cache_alloc(num_layers: int, num_blocks: int, block_size: int, num_kv_hea
                                _ptr(kb), _ptr(vb), scale_dtype, _ptr(k_pool), _ptr(v_pool),
                                ctypes.byref(out)))
     return out.value
+
+
+def kv_cache_alloc_typed(num_layers: int, num_blocks: int, block_size: int, num_kv_heads: int,
+                         head_dim: int, k_elem: int, v_elem: int, k_scales=None, v_scales=None,
+                         scale_dtype: int = DTYPE_F32, k_pool=None, v_pool=None) -> int:
+    """kv_cache_alloc with an element type per pool (ELEM_E4M3 or ELEM_BF16)."""
+    out = ctypes.c_void_p()
+    kb, vb = _scale_buffer(k_scales, scale_dtype), _scale_buffer(v_scales, scale_dtype)
+    _check(_lib.kv_cache_alloc_typed(num_layers, num_blocks, block_size, num_kv_heads, head_dim, k_elem,
+                                     v_elem, _ptr(kb), _ptr(vb), scale_dtype, _ptr(k_pool), _ptr(v_pool),
+                                     ctypes.byref(out)))
+    return out.value
+
+
+def kv_cache_elem_types(cache):
+    """(k_elem, v_elem) of a cache."""
+    k, v = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.kv_cache_elem_types(cache, ctypes.byref(k), ctypes.byref(v)))
+    return k.value, v.value
 
 
 def kv_cache_free(cache) -> None:

@@ -55,60 +55,78 @@ __device__ __forceinline__ void store_out(void *out, int64_t idx, float v, int b
         static_cast<float *>(out)[idx] = v;
 }
 
-template <int D>
+// Registers of one 32-token step of one lane: per 16-token tile, its D/4
+// elements of one key (K) and 4 keys x D/16 dims (V).  KB / VB are the pools'
+// element bytes: 1 (E4M3 codes) or 2 (bf16 values).
+template <int D, int KB, int VB>
 struct StepRegs {
-    static constexpr int NQ = D / 64;     // 16-byte loads per lane per tile (K and V each)
-    u32x4 k[2][NQ];
-    u32x4 v[2][NQ];
+    static constexpr int NK = D * KB / 64;     // 16-byte loads per lane per tile, K
+    static constexpr int NV = D * VB / 64;     // and V
+    u32x4 k[2][NK];
+    u32x4 v[2][NV];
     __device__ __forceinline__ uint32_t kw(int t, int j) const { return k[t][j >> 2][j & 3]; }
     __device__ __forceinline__ uint32_t vw(int t, int j) const { return v[t][j >> 2][j & 3]; }
 };
 
-// Loads of the K/V ring are issued as plain global_load_dwordx4 and waited for
-// explicitly (below): the compiler's own wait placement cannot see through the
-// ring and would drain every outstanding load at the loop head.
+// The all-E4M3 ring issues its loads as inline global_load_dwordx4 and waits
+// for them explicitly (below): the compiler's own wait placement drained
+// every outstanding load at the loop head.  That is only sound while the
+// register allocator neither copies nor spills a ring register between its
+// load and its wait, which a check of the built code confirms for those
+// kernels; the bf16 and mixed-type rings are heavier and use plain loads,
+// whose waits the compiler places itself.
+template <int KB, int VB>
+struct AsmRing { static constexpr bool ON = KB == 1 && VB == 1; };
+
+template <bool ASM>
 __device__ __forceinline__ void gload16(u32x4 &dst, const void *p) {
-    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst) : "v"(p) : "memory");
+    if constexpr (ASM)
+        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst) : "v"(p) : "memory");
+    else
+        dst = *reinterpret_cast<const u32x4 *>(p);
 }
 
 // Wait until at most N vector-memory loads are outstanding, then hand the
 // step's registers on: every register of the buffer is an operand of the
 // wait, so no use of it can be scheduled before the wait.
-template <int N, int D>
-__device__ __forceinline__ void wait_step(StepRegs<D> &r) {
+template <int N, int D, int KB, int VB>
+__device__ __forceinline__ void wait_step(StepRegs<D, KB, VB> &r) {
+    if constexpr (!AsmRing<KB, VB>::ON) return;
     asm volatile("s_waitcnt vmcnt(%1)" : "+v"(r.k[0][0]) : "n"(N) : "memory");
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int i = 0; i < StepRegs<D>::NQ; ++i) {
-            asm volatile("" : "+v"(r.k[t][i]));
-            asm volatile("" : "+v"(r.v[t][i]));
-        }
+        for (int i = 0; i < StepRegs<D, KB, VB>::NK; ++i) asm volatile("" : "+v"(r.k[t][i]));
+#pragma unroll
+        for (int i = 0; i < StepRegs<D, KB, VB>::NV; ++i) asm volatile("" : "+v"(r.v[t][i]));
+    }
 }
 
-// Issue the loads of one 32-token step: per lane, D/64 16-byte loads of K and
-// D/64 of V for each of the two 16-token tiles.  blk0 / blk1 are the pool
-// blocks of the two tiles.  A step past the wave's end (live == false) keeps
-// the same number of loads but points every lane at one shared 16-byte line,
-// so the ring stays branch-free without moving extra bytes.
-template <int D, int BS>
-__device__ __forceinline__ void load_step(StepRegs<D> &r, const uint8_t *k_pool, const uint8_t *v_pool,
+// Issue the loads of one 32-token step: per lane, for each of the two
+// 16-token tiles, the D/4 elements of key m in column quarter g (K) and keys
+// 4g..4g+3 of dims (D/16)m.. (V), as 16-byte loads.  blk0 / blk1 are the
+// pool blocks of the two tiles.  A step past the wave's end (live == false)
+// keeps the same number of loads but points every lane at one shared 16-byte
+// line, so the ring stays branch-free without moving extra bytes.
+template <int D, int BS, int KB, int VB>
+__device__ __forceinline__ void load_step(StepRegs<D, KB, VB> &r, const uint8_t *k_pool, const uint8_t *v_pool,
                                           uint32_t blk0, uint32_t blk1, int kv_heads, int kvh, int p,
                                           int m, int g, bool live) {
     constexpr int Q4 = D / 4;
-    constexpr int NQ = D / 64;
+    using R = StepRegs<D, KB, VB>;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const uint32_t blk = t == 0 ? blk0 : blk1;
         const int tb = (p + 16 * t) % BS;
-        const int64_t base = ((int64_t)blk * kv_heads + kvh) * (BS * D);
-        const uint8_t *kp = live ? k_pool + base + (g * BS + tb + m) * Q4 : k_pool;
-        const uint8_t *vp = live ? v_pool + base + ((tb / 4 + g) * D + (D / 16) * m) * 4 : k_pool;
+        const int64_t tile = ((int64_t)blk * kv_heads + kvh) * (BS * D);     // element index of the tile
+        const uint8_t *kp = live ? k_pool + (tile + (int64_t)(g * BS + tb + m) * Q4) * KB : k_pool;
+        const uint8_t *vp = live ? v_pool + (tile + (int64_t)((tb / 4 + g) * D + (D / 16) * m) * 4) * VB
+                                 : k_pool;
         const int inc = live ? 16 : 0;
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) gload16(r.k[t][i], kp + inc * i);
+        for (int i = 0; i < R::NK; ++i) gload16<AsmRing<KB, VB>::ON>(r.k[t][i], kp + inc * i);
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) gload16(r.v[t][i], vp + inc * i);
+        for (int i = 0; i < R::NV; ++i) gload16<AsmRing<KB, VB>::ON>(r.v[t][i], vp + inc * i);
     }
 }
 
@@ -122,11 +140,15 @@ struct SoftmaxState {
 };
 
 // One 32-token step of one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
-template <int D>
-__device__ __forceinline__ void compute_step(SoftmaxState<D> &st, StepRegs<D> &cur, const bf16x8 *qb,
+// E4M3 K codes become bf16 exactly; bf16 K words are the operand as they are.
+// E4M3 V codes become f16 exactly (P in f16); bf16 V uses the bf16 product
+// with P as a sum of two bf16 terms.
+template <int D, int KB, int VB>
+__device__ __forceinline__ void compute_step(SoftmaxState<D> &st, StepRegs<D, KB, VB> &cur, const bf16x8 *qb,
                                              int p, int c1, int g, float qk_scale) {
     constexpr int KK = D / 32;
     constexpr int MT = D / 16;
+    using R = StepRegs<D, KB, VB>;
     // ---- S^T = K Q^T for the two tiles
     f32x4 s[2];
 #pragma unroll
@@ -134,10 +156,15 @@ __device__ __forceinline__ void compute_step(SoftmaxState<D> &st, StepRegs<D> &c
         s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            const uint32_t w0 = cur.kw(t, 2 * kk), w1 = cur.kw(t, 2 * kk + 1);
-            const bf16x2 e0 = codes_to_bf16x2<false>(w0), e1 = codes_to_bf16x2<true>(w0);
-            const bf16x2 e2 = codes_to_bf16x2<false>(w1), e3 = codes_to_bf16x2<true>(w1);
-            const bf16x8 ka = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+            bf16x8 ka;
+            if constexpr (KB == 1) {
+                const uint32_t w0 = cur.kw(t, 2 * kk), w1 = cur.kw(t, 2 * kk + 1);
+                const bf16x2 e0 = codes_to_bf16x2<false>(w0), e1 = codes_to_bf16x2<true>(w0);
+                const bf16x2 e2 = codes_to_bf16x2<false>(w1), e3 = codes_to_bf16x2<true>(w1);
+                ka = bf16x8{e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+            } else {
+                ka = __builtin_bit_cast(bf16x8, cur.k[t][kk]);
+            }
             s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[kk], s[t], 0, 0, 0);
         }
     }
@@ -180,33 +207,66 @@ __device__ __forceinline__ void compute_step(SoftmaxState<D> &st, StepRegs<D> &c
     }
     st.run_sum += psum;
 
-    // ---- tail: codes of tokens past the end must not reach the product (NaN * 0)
+    // ---- tail: values of tokens past the end must not reach the product (NaN * 0)
     if (tail) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int valid = c1 - (p + 16 * t + 4 * g);          // tokens of this lane's group left
-            const uint32_t keep = valid >= 4 ? 0xFFFFFFFFu : valid <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * valid));
+            if constexpr (VB == 1) {
+                const uint32_t keep = valid >= 4 ? 0xFFFFFFFFu : valid <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * valid));
 #pragma unroll
-            for (int i = 0; i < StepRegs<D>::NQ; ++i) cur.v[t][i] &= keep;
+                for (int i = 0; i < R::NV; ++i) cur.v[t][i] &= keep;
+            } else {
+                // each dim's four tokens are two words: tokens (0, 1) and (2, 3)
+                const uint32_t keep0 = (valid > 0 ? 0x0000FFFFu : 0u) | (valid > 1 ? 0xFFFF0000u : 0u);
+                const uint32_t keep1 = (valid > 2 ? 0x0000FFFFu : 0u) | (valid > 3 ? 0xFFFF0000u : 0u);
+                const u32x4 keep = {keep0, keep1, keep0, keep1};
+#pragma unroll
+                for (int i = 0; i < R::NV; ++i) cur.v[t][i] &= keep;
+            }
         }
     }
 
     // ---- O^T += V^T P^T
-    const f16x8 pb = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3],
-                      (_Float16)pr[4], (_Float16)pr[5], (_Float16)pr[6], (_Float16)pr[7]};
+    if constexpr (VB == 1) {
+        const f16x8 pb = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3],
+                          (_Float16)pr[4], (_Float16)pr[5], (_Float16)pr[6], (_Float16)pr[7]};
 #pragma unroll
-    for (int j = 0; j < MT; ++j) {
-        const f16x2 e0 = codes_to_f16x2<false>(cur.vw(0, j)), e1 = codes_to_f16x2<true>(cur.vw(0, j));
-        const f16x2 e2 = codes_to_f16x2<false>(cur.vw(1, j)), e3 = codes_to_f16x2<true>(cur.vw(1, j));
-        const f16x8 va = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
-        st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, st.acc[j], 0, 0, 0);
+        for (int j = 0; j < MT; ++j) {
+            const f16x2 e0 = codes_to_f16x2<false>(cur.vw(0, j)), e1 = codes_to_f16x2<true>(cur.vw(0, j));
+            const f16x2 e2 = codes_to_f16x2<false>(cur.vw(1, j)), e3 = codes_to_f16x2<true>(cur.vw(1, j));
+            const f16x8 va = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+            st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, st.acc[j], 0, 0, 0);
+        }
+    } else {
+        // P as two bf16 terms, hi = bf16(P) and lo = bf16(P - hi): about 16
+        // significant bits, as precise as the f16 P of the E4M3 path (a single
+        // bf16 P keeps 8).  The extra products are free in this HBM-bound loop.
+        bf16x8 ph, pl;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            ph[i] = (__bf16)pr[i];
+            pl[i] = (__bf16)(pr[i] - (float)ph[i]);
+        }
+        // dim j's four tokens are words 2j, 2j+1 of each tile: half of vector j/2
+#pragma unroll
+        for (int j = 0; j < MT; j += 2) {
+            const u32x4 a = cur.v[0][j >> 1], b = cur.v[1][j >> 1];
+            const bf16x8 v0 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 4, 5));
+            const bf16x8 v1 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 2, 3, 6, 7));
+            st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, ph, st.acc[j], 0, 0, 0);
+            st.acc[j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, ph, st.acc[j + 1], 0, 0, 0);
+            st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pl, st.acc[j], 0, 0, 0);
+            st.acc[j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, pl, st.acc[j + 1], 0, 0, 0);
+        }
     }
 }
 
 // Register buffers in flight per wave: the step being computed plus
 // (NBUF - 1) steps whose loads are outstanding.
-template <int D>
-struct Depth { static constexpr int NBUF = D >= 256 ? 2 : 3; };
+// Three steps when one step's registers fit in 32 VGPRs, else two.
+template <int D, int KB, int VB>
+struct Depth { static constexpr int NBUF = 8 * (StepRegs<D, KB, VB>::NK + StepRegs<D, KB, VB>::NV) <= 32 ? 3 : 2; };
 
 // Workgroups are handed to the 8 XCDs round-robin by linear id, and each XCD
 // has its own CUs and L2.  Unit (pair p = seq * kv_heads + kv_head, split s)
@@ -225,11 +285,12 @@ __device__ __forceinline__ bool decode_unit(uint32_t h, const DecodeArgs &a, int
     return pair < pairs;
 }
 
-template <int D, int BS>
+template <int D, int BS, int KB, int VB>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     constexpr int KK = D / 32;     // QK^T instructions per tile
     constexpr int MT = D / 16;     // PV instructions per step (one per 16 dims)
-    constexpr int NBUF = Depth<D>::NBUF;
+    constexpr int NBUF = Depth<D, KB, VB>::NBUF;
+    using Regs = StepRegs<D, KB, VB>;
 
     extern __shared__ float smem[];   // [waves][G] max, [waves][G] sum, [waves][G][D] acc
 
@@ -296,28 +357,28 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int stride = kStep * kWaves;
     const int nsteps = c1 > c0 + kStep * wave ? (c1 - c0 - kStep * wave + stride - 1) / stride : 0;
     const int p0 = c0 + kStep * wave;
-    constexpr int LOADS = 4 * StepRegs<D>::NQ;      // loads per step
-    auto issue = [&](StepRegs<D> &r, int i) {
+    constexpr int LOADS = 2 * (Regs::NK + Regs::NV);   // loads per step
+    auto issue = [&](Regs &r, int i) {
         const bool live = i < nsteps;
         const int ii = live ? i : 0;
         const uint32_t b0 = __builtin_amdgcn_readlane(ids, 2 * ii);
         const uint32_t b1 = __builtin_amdgcn_readlane(ids, 2 * ii + 1);
-        load_step<D, BS>(r, a.k_pool, a.v_pool, b0, b1, a.kv_heads, kvh, p0 + ii * stride, m, g, live);
+        load_step<D, BS, KB, VB>(r, a.k_pool, a.v_pool, b0, b1, a.kv_heads, kvh, p0 + ii * stride, m, g, live);
     };
-    StepRegs<D> buf[NBUF];
+    Regs buf[NBUF];
     // Unconditional, so that every path into the loop holds the same loads in
     // flight (a wave with no steps issues dummy loads of one valid line).
 #pragma unroll
     for (int i = 0; i < NBUF - 1; ++i) issue(buf[i], i);
     for (int i = 0; i < nsteps; i += NBUF) {
-#pragma unroll
+#pragma clang loop unroll(full)
         for (int u = 0; u < NBUF; ++u) {
             const int step = i + u;
             if (step >= nsteps) break;
             // keep the next NBUF-1 steps' loads in flight while this one computes
             issue(buf[(u + NBUF - 1) % NBUF], step + NBUF - 1);
             wait_step<LOADS * (NBUF - 1)>(buf[u]);
-            compute_step<D>(st, buf[u], qb, p0 + step * stride, c1, g, a.qk_scale);
+            compute_step<D, KB, VB>(st, buf[u], qb, p0 + step * stride, c1, g, a.qk_scale);
         }
     }
     // Drain the ring.  The wait names every ring register, so none of them can
@@ -433,12 +494,12 @@ __global__ __launch_bounds__(D) void decode_reduce(DecodeArgs a) {
     store_out(a.out, ((int64_t)b * a.q_heads + head) * D + t, o, a.out_bf16);
 }
 
-template <int D, int BS>
+template <int D, int BS, int KB, int VB>
 hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     const int G = a.q_heads / a.kv_heads;
     const size_t smem = sizeof(float) * (size_t)kWaves * G * (2 + D);
     const uint32_t units = (uint32_t)a.splits * (uint32_t)(((a.num_seqs * a.kv_heads + 7) >> 3) << 3);
-    hipLaunchKernelGGL((decode_kernel<D, BS>), dim3(units), dim3(kThreads), smem, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, BS, KB, VB>), dim3(units), dim3(kThreads), smem, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     hipLaunchKernelGGL((decode_reduce<D>), dim3(a.q_heads, a.num_seqs), dim3(D), 0, stream, a);
@@ -482,15 +543,30 @@ void decode_plan(int32_t num_seqs, int32_t kv_heads, int32_t head_dim, int32_t b
     (void)block_size;
 }
 
+namespace {
+
+template <int D, int BS>
+hipError_t launch_decode_types(const DecodeArgs &a, hipStream_t stream) {
+    if (a.k_eb == 1 && a.v_eb == 1) return launch_decode_t<D, BS, 1, 1>(a, stream);
+    if constexpr (D <= 128) {     // bf16 pools: head_dim 64 and 128
+        if (a.k_eb == 1) return launch_decode_t<D, BS, 1, 2>(a, stream);
+        if (a.v_eb == 1) return launch_decode_t<D, BS, 2, 1>(a, stream);
+        return launch_decode_t<D, BS, 2, 2>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     if (a.block_size == 16) {
-        if (a.head_dim == 64) return launch_decode_t<64, 16>(a, stream);
-        if (a.head_dim == 128) return launch_decode_t<128, 16>(a, stream);
-        if (a.head_dim == 256) return launch_decode_t<256, 16>(a, stream);
+        if (a.head_dim == 64) return launch_decode_types<64, 16>(a, stream);
+        if (a.head_dim == 128) return launch_decode_types<128, 16>(a, stream);
+        if (a.head_dim == 256) return launch_decode_types<256, 16>(a, stream);
     } else if (a.block_size == 32) {
-        if (a.head_dim == 64) return launch_decode_t<64, 32>(a, stream);
-        if (a.head_dim == 128) return launch_decode_t<128, 32>(a, stream);
-        if (a.head_dim == 256) return launch_decode_t<256, 32>(a, stream);
+        if (a.head_dim == 64) return launch_decode_types<64, 32>(a, stream);
+        if (a.head_dim == 128) return launch_decode_types<128, 32>(a, stream);
+        if (a.head_dim == 256) return launch_decode_types<256, 32>(a, stream);
     }
     return hipErrorInvalidValue;
 }

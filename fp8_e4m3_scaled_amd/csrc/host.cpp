@@ -69,8 +69,10 @@ kvf8_status check_layer(const kvf8_cache *c, int32_t layer) {
     return KVF8_OK;
 }
 
-uint8_t *k_pool_of(const kvf8_cache *c, int32_t layer) { return c->k_base + (size_t)layer * c->pool_bytes; }
-uint8_t *v_pool_of(const kvf8_cache *c, int32_t layer) { return c->v_base + (size_t)layer * c->pool_bytes; }
+uint8_t *k_pool_of(const kvf8_cache *c, int32_t layer) { return c->k_base + (size_t)layer * c->k_pool_bytes; }
+uint8_t *v_pool_of(const kvf8_cache *c, int32_t layer) { return c->v_base + (size_t)layer * c->v_pool_bytes; }
+
+int32_t elem_bytes(kvf8_elem e) { return e == KVF8_ELEM_BF16 ? 2 : 1; }
 
 // splitmix64: the seeded generator behind kv_block_shuffle.
 uint64_t splitmix64(uint64_t &x) {
@@ -98,7 +100,17 @@ kvf8_status kv_cache_alloc(int32_t num_layers, int64_t num_blocks, int32_t block
                            int32_t num_kv_heads, int32_t head_dim, const void *k_scales,
                            const void *v_scales, kvf8_dtype scale_dtype, void *k_pool,
                            void *v_pool, kvf8_cache **out) {
+    return kv_cache_alloc_typed(num_layers, num_blocks, block_size, num_kv_heads, head_dim, KVF8_ELEM_E4M3,
+                                KVF8_ELEM_E4M3, k_scales, v_scales, scale_dtype, k_pool, v_pool, out);
+}
+
+kvf8_status kv_cache_alloc_typed(int32_t num_layers, int64_t num_blocks, int32_t block_size,
+                                 int32_t num_kv_heads, int32_t head_dim, kvf8_elem k_elem,
+                                 kvf8_elem v_elem, const void *k_scales, const void *v_scales,
+                                 kvf8_dtype scale_dtype, void *k_pool, void *v_pool, kvf8_cache **out) {
     if (!out) return fail(KVF8_E_INVALID, "out is NULL");
+    if ((k_elem != KVF8_ELEM_E4M3 && k_elem != KVF8_ELEM_BF16) || (v_elem != KVF8_ELEM_E4M3 && v_elem != KVF8_ELEM_BF16))
+        return fail(KVF8_E_INVALID, "k_elem and v_elem must be KVF8_ELEM_E4M3 or KVF8_ELEM_BF16");
     if (num_layers <= 0 || num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0)
         return fail(KVF8_E_INVALID, "num_layers, num_blocks, block_size, num_kv_heads and head_dim must be positive");
     if (num_blocks > INT32_MAX)
@@ -110,6 +122,8 @@ kvf8_status kv_cache_alloc(int32_t num_layers, int64_t num_blocks, int32_t block
         return fail(KVF8_E_INVALID, "scale_dtype must be KVF8_DTYPE_F32 or KVF8_DTYPE_BF16");
     if ((k_pool == nullptr) != (v_pool == nullptr))
         return fail(KVF8_E_INVALID, "k_pool and v_pool must both be NULL or both be given");
+    if ((k_elem == KVF8_ELEM_BF16 || v_elem == KVF8_ELEM_BF16) && head_dim > 128)
+        return fail(KVF8_E_UNSUPPORTED, "bf16 pools support head_dim 64 and 128, got %d", head_dim);
 
     std::vector<float> ks(num_layers, 1.0f), vs(num_layers, 1.0f);
     for (int32_t l = 0; l < num_layers; ++l) {
@@ -121,11 +135,17 @@ kvf8_status kv_cache_alloc(int32_t num_layers, int64_t num_blocks, int32_t block
         if (!scale_usable(vs[l]))
             return fail(KVF8_E_SCALE, "FP8 cache scale of layer %d (V) must be finite and nonzero with a finite reciprocal, got %g",
                         l, (double)vs[l]);
+        if (k_elem == KVF8_ELEM_BF16 && ks[l] != 1.0f)
+            return fail(KVF8_E_SCALE, "the bf16 K pool stores values as given: its scale (layer %d) must be 1, got %g",
+                        l, (double)ks[l]);
+        if (v_elem == KVF8_ELEM_BF16 && vs[l] != 1.0f)
+            return fail(KVF8_E_SCALE, "the bf16 V pool stores values as given: its scale (layer %d) must be 1, got %g",
+                        l, (double)vs[l]);
     }
 
     const size_t tile = (size_t)block_size * (size_t)head_dim;
-    const size_t pool_bytes = (size_t)num_blocks * (size_t)num_kv_heads * tile;
-    if (pool_bytes / tile / (size_t)num_kv_heads != (size_t)num_blocks)
+    const size_t pool_elems = (size_t)num_blocks * (size_t)num_kv_heads * tile;
+    if (pool_elems / tile / (size_t)num_kv_heads != (size_t)num_blocks)
         return fail(KVF8_E_INVALID, "pool size overflows");
 
     kvf8_cache *c = new (std::nothrow) kvf8_cache();
@@ -135,7 +155,10 @@ kvf8_status kv_cache_alloc(int32_t num_layers, int64_t num_blocks, int32_t block
     c->block_size = block_size;
     c->kv_heads = num_kv_heads;
     c->head_dim = head_dim;
-    c->pool_bytes = pool_bytes;
+    c->k_eb = elem_bytes(k_elem);
+    c->v_eb = elem_bytes(v_elem);
+    c->k_pool_bytes = pool_elems * (size_t)c->k_eb;
+    c->v_pool_bytes = pool_elems * (size_t)c->v_eb;
     c->k_scale = ks;
     c->v_scale = vs;
     c->k_inv.resize(num_layers);
@@ -165,18 +188,19 @@ kvf8_status kv_cache_alloc(int32_t num_layers, int64_t num_blocks, int32_t block
         delete c;
         return hip_fail(e, "hipGetDevice");
     }
-    const size_t total = pool_bytes * (size_t)num_layers;
-    e = hipMalloc(reinterpret_cast<void **>(&c->k_base), total);
-    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&c->v_base), total);
-    if (e == hipSuccess) e = hipMemset(c->k_base, 0, total);
-    if (e == hipSuccess) e = hipMemset(c->v_base, 0, total);
+    const size_t k_total = c->k_pool_bytes * (size_t)num_layers;
+    const size_t v_total = c->v_pool_bytes * (size_t)num_layers;
+    e = hipMalloc(reinterpret_cast<void **>(&c->k_base), k_total);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&c->v_base), v_total);
+    if (e == hipSuccess) e = hipMemset(c->k_base, 0, k_total);
+    if (e == hipSuccess) e = hipMemset(c->v_base, 0, v_total);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         const bool oom = e == hipErrorOutOfMemory;
         if (c->k_base) (void)hipFree(c->k_base);
         if (c->v_base) (void)hipFree(c->v_base);
         delete c;
-        if (oom) return fail(KVF8_E_NOMEM, "device allocation of 2 x %zu pool bytes failed", total);
+        if (oom) return fail(KVF8_E_NOMEM, "device allocation of %zu + %zu pool bytes failed", k_total, v_total);
         return hip_fail(e, "allocating and clearing the pools");
     }
     c->owned = true;
@@ -212,6 +236,10 @@ kvf8_status kv_cache_set_scales(kvf8_cache *c, int32_t layer, const void *k_scal
     if (!scale_usable(vs))
         return fail(KVF8_E_SCALE, "FP8 cache scale of layer %d (V) must be finite and nonzero with a finite reciprocal, got %g",
                     layer, (double)vs);
+    if (c->k_eb == 2 && ks != 1.0f)
+        return fail(KVF8_E_SCALE, "the bf16 K pool stores values as given: its scale must be 1, got %g", (double)ks);
+    if (c->v_eb == 2 && vs != 1.0f)
+        return fail(KVF8_E_SCALE, "the bf16 V pool stores values as given: its scale must be 1, got %g", (double)vs);
     c->k_scale[layer] = ks;
     c->v_scale[layer] = vs;
     c->k_inv[layer] = 1.0f / ks;
@@ -233,7 +261,14 @@ kvf8_status kv_cache_pools(const kvf8_cache *c, int32_t layer, uint8_t **k_pool,
     if (st != KVF8_OK) return st;
     if (k_pool) *k_pool = k_pool_of(c, layer);
     if (v_pool) *v_pool = v_pool_of(c, layer);
-    if (pool_bytes) *pool_bytes = c->pool_bytes;
+    if (pool_bytes) *pool_bytes = c->k_pool_bytes;
+    return ok();
+}
+
+kvf8_status kv_cache_elem_types(const kvf8_cache *c, kvf8_elem *k_elem, kvf8_elem *v_elem) {
+    if (!c) return fail(KVF8_E_INVALID, "cache is NULL");
+    if (k_elem) *k_elem = c->k_eb == 2 ? KVF8_ELEM_BF16 : KVF8_ELEM_E4M3;
+    if (v_elem) *v_elem = c->v_eb == 2 ? KVF8_ELEM_BF16 : KVF8_ELEM_E4M3;
     return ok();
 }
 
@@ -322,6 +357,8 @@ kvf8_status kv_store_fp8(kvf8_cache *c, int32_t layer, const uint16_t *k_bf16,
     a.v_pool = v_pool_of(c, layer);
     a.k_inv = c->k_inv[layer];
     a.v_inv = c->v_inv[layer];
+    a.k_eb = c->k_eb;
+    a.v_eb = c->v_eb;
     a.kv_heads = c->kv_heads;
     a.head_dim = c->head_dim;
     a.block_size = c->block_size;
@@ -397,6 +434,8 @@ kvf8_status paged_attn_decode(kvf8_cache *c, int32_t layer, const uint16_t *q_bf
                     (double)a.qk_scale);
     a.v_scale = c->v_scale[layer];
     a.out_bf16 = out_dtype == KVF8_DTYPE_BF16;
+    a.k_eb = c->k_eb;
+    a.v_eb = c->v_eb;
     hipError_t e = kvf8::launch_decode(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "paged_attn_decode launch");
     return ok();
@@ -410,6 +449,8 @@ kvf8_status paged_attn_prefill_chunk(kvf8_cache *c, int32_t layer, const uint16_
                                      void *out, kvf8_dtype out_dtype, void *stream) {
     kvf8_status st = check_layer(c, layer);
     if (st != KVF8_OK) return st;
+    if (c->k_eb != 1 || c->v_eb != 1)
+        return fail(KVF8_E_UNSUPPORTED, "paged_attn_prefill_chunk needs E4M3 K and V pools");
     if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_ctx_len < 0 || max_blocks_per_seq < 0)
         return fail(KVF8_E_INVALID, "sizes must be >= 0");
     if (num_q_heads <= 0 || num_q_heads % c->kv_heads != 0)
@@ -474,6 +515,7 @@ kvf8_status kv_shift_rope(kvf8_cache *c, int32_t layer, const int64_t *slots, in
         return fail(KVF8_E_INVALID, "theta_base must be finite and > 0");
     if (style != KVF8_ROPE_NORM && style != KVF8_ROPE_NEOX)
         return fail(KVF8_E_INVALID, "style must be KVF8_ROPE_NORM or KVF8_ROPE_NEOX");
+    if (c->k_eb != 1) return fail(KVF8_E_UNSUPPORTED, "kv_shift_rope needs an E4M3 K pool");
     if (n_slots == 0) return ok();
     if (!slots) return fail(KVF8_E_INVALID, "slots is NULL");
     kvf8::KShiftArgs a{};

@@ -13,7 +13,10 @@ struct kvf8_cache {
     int32_t block_size = 0;
     int32_t kv_heads = 0;
     int32_t head_dim = 0;
-    size_t pool_bytes = 0;          // bytes of one layer's K pool (same for V)
+    int32_t k_eb = 1;               // element bytes of the K pool: 1 (E4M3) or 2 (bf16)
+    int32_t v_eb = 1;
+    size_t k_pool_bytes = 0;        // bytes of one layer's K pool
+    size_t v_pool_bytes = 0;
     uint8_t *k_base = nullptr;      // [layers][pool_bytes]
     uint8_t *v_base = nullptr;
     bool owned = false;
@@ -41,6 +44,8 @@ struct StoreArgs {
     int32_t kv_heads;
     int32_t head_dim;
     int32_t block_size;
+    int32_t k_eb;            // element bytes of the K pool: 1 (E4M3 codes) or 2 (bf16 as given)
+    int32_t v_eb;
 };
 hipError_t launch_store(const StoreArgs &a, hipStream_t stream);
 
@@ -65,6 +70,8 @@ struct DecodeArgs {
     float qk_scale;          // k_scale * sm_scale * log2(e)
     float v_scale;
     int32_t out_bf16;
+    int32_t k_eb;            // element bytes of the K / V pools: 1 (E4M3) or 2 (bf16)
+    int32_t v_eb;
 };
 // Number of splits and chunk length the decode uses for this shape.
 constexpr int kDecodeThreads = 256;   // threads per decode workgroup (4 waves)

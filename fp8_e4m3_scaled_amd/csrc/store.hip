@@ -15,6 +15,8 @@
 //      common case of prefill and fills), four dims x four tokens are 16
 //      consecutive bytes -> one 16-byte store.  Otherwise each token's V byte
 //      is written on its own (the decode-step case of one token per sequence).
+// A bf16 pool gets the input bits at the same element positions (two bytes
+// each): 32-byte runs for K and for a V group, two-byte writes otherwise.
 
 #include "fp8_device.hpp"
 #include "internal.hpp"
@@ -25,6 +27,9 @@ namespace {
 constexpr int kStoreThreads = 256;
 constexpr int kGroups = 1;          // four-token groups per workgroup
 
+// KB / VB: element bytes of the K / V pool, 1 (E4M3 codes) or 2 (the bf16
+// values as given, at the same element positions).
+template <int KB, int VB>
 __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a) {
     const int D = a.head_dim;
     const int H = a.kv_heads;
@@ -61,19 +66,25 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a) {
             if (s < 0) continue;
             const u32x4 *src = reinterpret_cast<const u32x4 *>(kin + (tok0 + k) * a.k_stride + (int64_t)h * D + r * 16);
             const u32x4 lo = src[0], hi = src[1];
-            const uint32_t w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            u32x4 out;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t p0 = w[2 * j], p1 = w[2 * j + 1];
-                out[j] = encode4(scaled(p0 & 0xFFFF, a.k_inv), scaled(p0 >> 16, a.k_inv),
-                                 scaled(p1 & 0xFFFF, a.k_inv), scaled(p1 >> 16, a.k_inv));
-            }
             const int64_t blk = s / BS;
             const int t = (int)(s - blk * BS);
             const int d0 = r * 16;
             const int64_t off = (blk * H + h) * tile + ((int64_t)(d0 / quarter) * BS + t) * quarter + d0 % quarter;
-            *reinterpret_cast<u32x4 *>(kout + off) = out;
+            if constexpr (KB == 1) {
+                const uint32_t w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                u32x4 out;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t p0 = w[2 * j], p1 = w[2 * j + 1];
+                    out[j] = encode4(scaled(p0 & 0xFFFF, a.k_inv), scaled(p0 >> 16, a.k_inv),
+                                     scaled(p1 & 0xFFFF, a.k_inv), scaled(p1 >> 16, a.k_inv));
+                }
+                *reinterpret_cast<u32x4 *>(kout + off) = out;
+            } else {
+                u32x4 *dst = reinterpret_cast<u32x4 *>(kout + 2 * off);
+                dst[0] = lo;
+                dst[1] = hi;
+            }
         }
 
         // ---------------- V
@@ -86,21 +97,38 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a) {
             for (int it = threadIdx.x; it < v_items; it += kStoreThreads) {
                 const int h = it / quads;
                 const int d4 = it - h * quads;
-                float y[4][4];   // [token][dim]
+                uint32_t b[4][4];   // [token][dim] bf16 bits
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const uint2 w = *reinterpret_cast<const uint2 *>(vin + (tok0 + k) * a.v_stride +
                                                                      (int64_t)h * D + d4 * 4);
-                    y[k][0] = scaled(w.x & 0xFFFF, a.v_inv);
-                    y[k][1] = scaled(w.x >> 16, a.v_inv);
-                    y[k][2] = scaled(w.y & 0xFFFF, a.v_inv);
-                    y[k][3] = scaled(w.y >> 16, a.v_inv);
+                    b[k][0] = w.x & 0xFFFF;
+                    b[k][1] = w.x >> 16;
+                    b[k][2] = w.y & 0xFFFF;
+                    b[k][3] = w.y >> 16;
                 }
-                u32x4 out;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) out[j] = encode4(y[0][j], y[1][j], y[2][j], y[3][j]);
                 const int64_t off = (blk * H + h) * tile + ((int64_t)(t0 >> 2) * D + d4 * 4) * 4;
-                *reinterpret_cast<u32x4 *>(vout + off) = out;
+                if constexpr (VB == 1) {
+                    u32x4 out;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        out[j] = encode4(scaled(b[0][j], a.v_inv), scaled(b[1][j], a.v_inv),
+                                         scaled(b[2][j], a.v_inv), scaled(b[3][j], a.v_inv));
+                    *reinterpret_cast<u32x4 *>(vout + off) = out;
+                } else {
+                    // dim j: tokens 0..3 as four consecutive bf16 values
+                    u32x4 o0, o1;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        o0[2 * j] = b[0][j] | (b[1][j] << 16);
+                        o0[2 * j + 1] = b[2][j] | (b[3][j] << 16);
+                        o1[2 * j] = b[0][j + 2] | (b[1][j + 2] << 16);
+                        o1[2 * j + 1] = b[2][j + 2] | (b[3][j + 2] << 16);
+                    }
+                    u32x4 *dst = reinterpret_cast<u32x4 *>(vout + 2 * off);
+                    dst[0] = o0;
+                    dst[1] = o1;
+                }
             }
         } else {
             // one token at a time: its four codes sit 4 bytes apart
@@ -113,15 +141,24 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a) {
                 if (s < 0) continue;
                 const uint2 w = *reinterpret_cast<const uint2 *>(vin + (tok0 + k) * a.v_stride +
                                                                  (int64_t)h * D + d4 * 4);
-                const uint32_t c = encode4(scaled(w.x & 0xFFFF, a.v_inv), scaled(w.x >> 16, a.v_inv),
-                                           scaled(w.y & 0xFFFF, a.v_inv), scaled(w.y >> 16, a.v_inv));
                 const int64_t blk = s / BS;
                 const int t = (int)(s - blk * BS);
-                uint8_t *dst = vout + (blk * H + h) * tile + ((int64_t)(t >> 2) * D + d4 * 4) * 4 + (t & 3);
-                dst[0] = (uint8_t)(c & 0xFF);
-                dst[4] = (uint8_t)((c >> 8) & 0xFF);
-                dst[8] = (uint8_t)((c >> 16) & 0xFF);
-                dst[12] = (uint8_t)(c >> 24);
+                const int64_t e = (blk * H + h) * tile + ((int64_t)(t >> 2) * D + d4 * 4) * 4 + (t & 3);
+                if constexpr (VB == 1) {
+                    const uint32_t c = encode4(scaled(w.x & 0xFFFF, a.v_inv), scaled(w.x >> 16, a.v_inv),
+                                               scaled(w.y & 0xFFFF, a.v_inv), scaled(w.y >> 16, a.v_inv));
+                    uint8_t *dst = vout + e;
+                    dst[0] = (uint8_t)(c & 0xFF);
+                    dst[4] = (uint8_t)((c >> 8) & 0xFF);
+                    dst[8] = (uint8_t)((c >> 16) & 0xFF);
+                    dst[12] = (uint8_t)(c >> 24);
+                } else {
+                    uint16_t *dst = reinterpret_cast<uint16_t *>(vout) + e;
+                    dst[0] = (uint16_t)(w.x & 0xFFFF);
+                    dst[4] = (uint16_t)(w.x >> 16);
+                    dst[8] = (uint16_t)(w.y & 0xFFFF);
+                    dst[12] = (uint16_t)(w.y >> 16);
+                }
             }
         }
     }
@@ -132,7 +169,14 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a) {
 hipError_t launch_store(const StoreArgs &a, hipStream_t stream) {
     const int64_t wgs = (a.num_tokens + 4 * kGroups - 1) / (4 * kGroups);
     if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(store_kernel, dim3((unsigned)wgs), dim3(kStoreThreads), 0, stream, a);
+    if (a.k_eb == 1 && a.v_eb == 1)
+        hipLaunchKernelGGL((store_kernel<1, 1>), dim3((unsigned)wgs), dim3(kStoreThreads), 0, stream, a);
+    else if (a.k_eb == 1)
+        hipLaunchKernelGGL((store_kernel<1, 2>), dim3((unsigned)wgs), dim3(kStoreThreads), 0, stream, a);
+    else if (a.v_eb == 1)
+        hipLaunchKernelGGL((store_kernel<2, 1>), dim3((unsigned)wgs), dim3(kStoreThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((store_kernel<2, 2>), dim3((unsigned)wgs), dim3(kStoreThreads), 0, stream, a);
     return hipGetLastError();
 }
 

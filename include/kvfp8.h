@@ -61,6 +61,15 @@ typedef enum kvf8_dtype {
     KVF8_DTYPE_BF16 = 1
 } kvf8_dtype;
 
+/* Element type of one pool.  E4M3 is the scaled FP8 cache; BF16 stores the
+ * given bf16 values as they are (the two-byte twin) [P3, "What turning it
+ * on costs": the fp8-vs-bf16 exchange rate; P1, tests/test-fp8.cpp and
+ * test-backend-ops.cpp choose the K and V cache types independently]. */
+typedef enum kvf8_elem {
+    KVF8_ELEM_E4M3 = 0,
+    KVF8_ELEM_BF16 = 1
+} kvf8_elem;
+
 typedef enum kvf8_rope {
     KVF8_ROPE_NORM = 0,      /* rotary pairs (2i, 2i+1)                          */
     KVF8_ROPE_NEOX = 1       /* rotary pairs (i, i + rot_dim/2)                  */
@@ -113,6 +122,26 @@ kvf8_status kv_cache_alloc(int32_t num_layers, int64_t num_blocks, int32_t block
                            const void *k_scales, const void *v_scales, kvf8_dtype scale_dtype,
                            void *k_pool, void *v_pool, kvf8_cache **out);
 
+/*
+ * kv_cache_alloc with an element type per pool: k_elem / v_elem in
+ * {KVF8_ELEM_E4M3, KVF8_ELEM_BF16} (kv_cache_alloc is E4M3 / E4M3).  A BF16
+ * pool holds num_layers * num_blocks * block_size * num_kv_heads * head_dim
+ * bf16 values in the same tile order as above (element (t, d) at the same
+ * index, two bytes each) and stores the given values unchanged, so its scale
+ * must be 1.0 for every layer (NULL scales give 1.0; any other value ->
+ * KVF8_E_SCALE).  BF16 pools support head_dim 64 and 128 (256 ->
+ * KVF8_E_UNSUPPORTED).  paged_attn_prefill_chunk needs both pools E4M3 and
+ * kv_shift_rope needs an E4M3 K pool (else KVF8_E_UNSUPPORTED).
+ */
+kvf8_status kv_cache_alloc_typed(int32_t num_layers, int64_t num_blocks, int32_t block_size,
+                                 int32_t num_kv_heads, int32_t head_dim, kvf8_elem k_elem,
+                                 kvf8_elem v_elem, const void *k_scales, const void *v_scales,
+                                 kvf8_dtype scale_dtype, void *k_pool, void *v_pool,
+                                 kvf8_cache **out);
+
+/* The element types of a cache's K and V pools (host outputs; either may be NULL). */
+kvf8_status kv_cache_elem_types(const kvf8_cache *cache, kvf8_elem *k_elem, kvf8_elem *v_elem);
+
 /* Destroy a cache; frees what kv_cache_alloc allocated.  NULL -> KVF8_OK. */
 kvf8_status kv_cache_free(kvf8_cache *cache);
 
@@ -126,8 +155,9 @@ kvf8_status kv_cache_set_scales(kvf8_cache *cache, int32_t layer, const void *k_
 kvf8_status kv_cache_get_scales(const kvf8_cache *cache, int32_t layer, float *k_scale,
                                 float *v_scale);
 
-/* Borrowed device views of one layer's pools and their size in bytes each
- * (outputs may be NULL). */
+/* Borrowed device views of one layer's pools and the size in bytes of the K
+ * pool (outputs may be NULL; the V pool's size is the same times its element
+ * size over K's). */
 kvf8_status kv_cache_pools(const kvf8_cache *cache, int32_t layer, uint8_t **k_pool,
                            uint8_t **v_pool, size_t *pool_bytes);
 
@@ -159,7 +189,8 @@ kvf8_status kv_block_shuffle(kvf8_cache *cache, uint64_t seed);
  * signed zero follow [P2, ggml_fp32_to_f8_e4m3]: NaN -> sign|0x7F with the
  * input's sign, +-Inf and |y| >= 448 -> sign|0x7E, zero keeps its sign.
  * The division of [P1, build_attn_scale_kv_inputs] (store K/s, V/s) is done
- * as a multiply by the reciprocal.
+ * as a multiply by the reciprocal.  A BF16 pool (kv_cache_alloc_typed)
+ * receives the bf16 bit patterns unchanged instead.
  *
  * k_bf16, v_bf16 (device): [num_tokens][num_kv_heads][head_dim] bf16 rows;
  *   row i starts at element i * k_tok_stride (resp. v_tok_stride), heads and

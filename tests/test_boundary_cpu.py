@@ -259,3 +259,42 @@ def test_read_probe_host_checks():
     with pytest.raises(kv.KvF8Error) as ei:
         kv.kvf8_read_probe(1 << 30, 64, None, 8, 0)
     assert ei.value.status == kv.E_INVALID
+
+
+def test_typed_pools_host_rules():
+    """Per-pool element types: bf16 pools keep scale 1, support head_dim <= 128, report
+    their types and byte sizes, and the E4M3-only calls refuse them before any launch."""
+    E, B = kv.ELEM_E4M3, kv.ELEM_BF16
+    with pytest.raises(kv.KvF8Error) as ei:
+        kv.kv_cache_alloc_typed(1, 8, 16, 2, 64, B, E, [0.5], [0.5], kv.DTYPE_F32, FAKE_K, FAKE_V)
+    assert ei.value.status == kv.E_SCALE                                   # bf16 K pool scale != 1
+    with pytest.raises(kv.KvF8Error) as ei:
+        kv.kv_cache_alloc_typed(1, 8, 16, 2, 256, E, B, None, None, kv.DTYPE_F32, FAKE_K, FAKE_V)
+    assert ei.value.status == kv.E_UNSUPPORTED
+    with pytest.raises(kv.KvF8Error) as ei:
+        kv.kv_cache_alloc_typed(1, 8, 16, 2, 64, 7, E, None, None, kv.DTYPE_F32, FAKE_K, FAKE_V)
+    assert ei.value.status == kv.E_INVALID
+    for ke, ve in [(E, E), (E, B), (B, E), (B, B)]:
+        c = kv.kv_cache_alloc_typed(2, 8, 16, 2, 64, ke, ve, [0.5, 1.0] if ke == E else None,
+                                    [0.25, 1.0] if ve == E else None, kv.DTYPE_F32, FAKE_K, FAKE_V)
+        try:
+            assert kv.kv_cache_elem_types(c) == (ke, ve)
+            k0, v0, nbytes = kv.kv_cache_pools(c, 0)
+            k1, v1, _ = kv.kv_cache_pools(c, 1)
+            ke_b, ve_b = (2 if ke == B else 1), (2 if ve == B else 1)
+            assert nbytes == 8 * 2 * 16 * 64 * ke_b
+            assert k1 - k0 == 8 * 2 * 16 * 64 * ke_b and v1 - v0 == 8 * 2 * 16 * 64 * ve_b
+            if ke == B:
+                with pytest.raises(kv.KvF8Error) as ei:
+                    kv.kv_cache_set_scales(c, 0, 2.0, None)
+                assert ei.value.status == kv.E_SCALE
+                with pytest.raises(kv.KvF8Error) as ei:
+                    kv.kv_shift_rope(c, 0, 1 << 30, 4, -1, 1e4, 64, kv.ROPE_NEOX, 0)
+                assert ei.value.status == kv.E_UNSUPPORTED
+            if (ke, ve) != (E, E):
+                with pytest.raises(kv.KvF8Error) as ei:
+                    kv.paged_attn_prefill_chunk(c, 0, 1 << 30, 4, 1 << 30, 1 << 30, 1 << 30, 4, 1, 8, 8,
+                                                16, 0.125, 1 << 30, kv.DTYPE_F32, 0)
+                assert ei.value.status == kv.E_UNSUPPORTED
+        finally:
+            kv.kv_cache_free(c)
