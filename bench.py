@@ -211,19 +211,78 @@ def run_llama8b(args):
                      "frac_hbm_peak": round(store_gbps / HBM_PEAK_GBPS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(decode_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(decode_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "decode_kernel<128,16>",
+                     "traffic": traffic, "kernel": "decode_kernel<128,16,1,1>",
                      "kernel_source_sha": kernel_sha},
         "wall_s_timed": round(wall, 3),
     }
 
     result["stream_read_ceiling"] = _stream_ceiling(kv, stream)
     result["decode"]["frac_of_stream_ceiling"] = round(decode_gbps / result["stream_read_ceiling"]["GBps"], 4)
+    for h in handles:
+        kv.kv_cache_free(h)
+    handles = []
+    del pools
+    torch.cuda.empty_cache()
+    result["element_types"] = _typed_exchange(args, kv, w, K, V, slots_d, T, q, tables, lens, max_len, out,
+                                              ks, vs, de_mean, stream)
     if args.cpu_seconds > 0:
         result["cpu_baseline"], result["parity_sample"] = _cpu_baseline(
             w, K, V, slots, q, out, ks, vs, args.cpu_seconds)
-    for h in handles:
-        kv.kv_cache_free(h)
     return result
+
+
+def _typed_exchange(args, kv, w, K, V, slots_d, T, q, tables, lens, max_len, out, ks, vs, fp8_ms, stream):
+    """The same decode over caches whose pools hold bf16 values instead of E4M3
+    codes (the bf16 twin, and the two mixed K/V combinations), on the same
+    inputs and shape: the decode time of each and the exchange rate, the E4M3
+    cache's decode throughput over the other's.  Algorithmic bytes count each
+    pool at its own element size."""
+    import torch
+    E, B = kv.ELEM_E4M3, kv.ELEM_BF16
+    row = w.Hkv * w.D
+    n = w.NB * w.Hkv * w.BS * w.D
+    kv_tokens = int(w.total_lengths.sum())
+    blocks = int(sum(-(-int(L) // w.BS) for L in w.total_lengths))
+    out = torch.empty_like(out)   # the E4M3 decode's output stays intact for the parity sample
+    res = {}
+    for name, ke, ve in (("bf16_twin", B, B), ("k_e4m3_v_bf16", E, B), ("k_bf16_v_e4m3", B, E)):
+        keb, veb = (1 if ke == E else 2), (1 if ve == E else 2)
+        hs, pools = [], []
+        for _ in range(3):
+            kp = torch.zeros(n * keb, dtype=torch.uint8, device=K.device)
+            vp = torch.zeros(n * veb, dtype=torch.uint8, device=K.device)
+            h = kv.kv_cache_alloc_typed(1, w.NB, w.BS, w.Hkv, w.D, ke, ve,
+                                        [float(ks) if ke == E else 1.0], [float(vs) if ve == E else 1.0],
+                                        kv.DTYPE_F32, kp, vp)
+            kv.kv_store_fp8(h, 0, K, V, row, row, slots_d, T, stream)
+            hs.append(h)
+            pools.append((kp, vp))
+        ws_bytes = kv.paged_attn_decode_workspace(hs[0], w.B, w.Hq, max_len)
+        ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=K.device)
+        torch.cuda.synchronize()
+
+        def decode(i):
+            kv.paged_attn_decode(hs[(i + 1) % 3], 0, q, w.Hq, tables, w.max_blocks, lens, w.B, max_len,
+                                 w.sm_scale(), out, kv.DTYPE_BF16, ws, ws_bytes, stream)
+
+        for i in range(args.warmup):
+            decode(i)
+        ev = []
+        for i in range(args.steps):
+            _time_ms(lambda: decode(i), stream, ev)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        nbytes = kv_tokens * w.Hkv * w.D * (keb + veb) + w.B * w.Hq * w.D * 4 + 4 * blocks + 4 * w.B
+        res[name] = {"k_elem": "e4m3" if ke == E else "bf16", "v_elem": "e4m3" if ve == E else "bf16",
+                     "ms_mean": round(ms, 5), "algorithmic_bytes": nbytes,
+                     "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "tokens_per_s": round(w.B / (ms * 1e-3), 1),
+                     "e4m3_speedup": round(ms / fp8_ms, 4)}
+        for h in hs:
+            kv.kv_cache_free(h)
+        del pools, ws
+        torch.cuda.empty_cache()
+    return res
 
 
 def _stream_ceiling(kv, stream, nbytes=2 << 30, launches=20):
@@ -536,7 +595,7 @@ def run_longctx(args):
                            tokens_per_s=round(nsl / (sh.mean() * 1e-3), 1))
     res["roofline"] = {"bound": "hbm", "achieved": round(de_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                        "frac": round(de_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                       "kernel": "decode_kernel<256,32> + decode_reduce<256>"}
+                       "kernel": "decode_kernel<256,32,1,1> + decode_reduce<256>"}
     for h in handles:
         kv.kv_cache_free(h)
     return res
@@ -590,7 +649,7 @@ def run_varlen(args):
     res["kv_store"] = dict(_stats(st), tokens=w.B, tokens_per_s=round(w.B / (st.mean() * 1e-3), 1))
     res["roofline"] = {"bound": "hbm", "achieved": round(de_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                        "frac": round(de_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                       "kernel": "decode_kernel<128,16> + decode_reduce<128>"}
+                       "kernel": "decode_kernel<128,16,1,1> + decode_reduce<128>"}
     kv.kv_cache_free(h)
     return res
 
