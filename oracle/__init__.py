@@ -18,6 +18,10 @@ Parity status of each function (what pins it is in ``tests/test_oracle_*``):
   kshift                      pinned (complex rotation in NumPy, delta 0,
                               angle pins)
   kv_bytes_per_block          pinned (exact halving)
+  amax / calibrate_scales     pinned (torch's abs-max, planted maxima and NaN,
+                              power-of-two amax, fp64-then-fp32 division,
+                              torch's bf16 rounding, the calibrated maximum
+                              encodes to the top finite E4M3 code)
 """
 from __future__ import annotations
 
@@ -88,6 +92,9 @@ def _load():
         "orc_kshift": (ctypes.c_int, [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, P, i64,
                                       ctypes.c_int, f32, ctypes.c_int, ctypes.c_int]),
         "orc_kv_bytes_per_block": (i64, [ctypes.c_int] * 4),
+        "orc_amax_bf16": (f32, [P, i64, i64, i64, f32]),
+        "orc_scale_from_amax": (f32, [f32]),
+        "orc_f32_to_bf16_rne": (ctypes.c_uint16, [f32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -133,6 +140,49 @@ def scale_ok(s: float) -> bool:
 
 def scale_inverse(s: float) -> np.float32:
     return np.float32(_load().orc_scale_inverse(float(np.float32(s))))
+
+
+# ---------------------------------------------------------------- calibration
+def amax(bits, row_elems: int | None = None, start: float = 0.0) -> np.float32:
+    """Running amax of bf16 bits: 2-D [rows][stride] (only the first row_elems
+    of each row count) or any shape (all elements count), from `start`."""
+    b = np.asarray(bits, np.uint16)
+    if b.ndim != 2:
+        b = b.reshape(1, -1) if b.size else b.reshape(0, 1)
+    b = np.ascontiguousarray(b)
+    rows, stride = b.shape
+    n = stride if row_elems is None else int(row_elems)
+    assert 0 <= n <= stride
+    return np.float32(_load().orc_amax_bf16(_ptr(b), rows, n, stride, float(np.float32(start))))
+
+
+def scale_from_amax(a: float) -> np.float32:
+    """fp32 scale amax / 448."""
+    return np.float32(_load().orc_scale_from_amax(float(np.float32(a))))
+
+
+def f32_to_bf16(x) -> np.ndarray:
+    """Nearest-even bf16 bits of fp32 values (any shape)."""
+    a = np.asarray(x, np.float32)
+    f = _load().orc_f32_to_bf16_rne
+    return np.array([f(float(v)) for v in a.reshape(-1)], np.uint16).reshape(a.shape)
+
+
+def calibrate_scales(k_amax: float, v_amax: float, scale_dtype: str = "f32"):
+    """(k, v) scales as fp32 values and as the bits of scale_dtype ("f32" ->
+    uint32 fp32 bits, NaN as 0x7FC00000; "bf16" -> uint16 bf16 bits)."""
+    out_v, out_b = [], []
+    for a in (k_amax, v_amax):
+        s = scale_from_amax(a)
+        if scale_dtype == "bf16":
+            b = np.uint16(f32_to_bf16(s))
+            v = np.array([np.uint32(b) << np.uint32(16)], np.uint32).view(np.float32)[0]
+        else:
+            b = np.uint32(0x7FC00000) if np.isnan(s) else np.array([s], np.float32).view(np.uint32)[0]
+            v = s
+        out_v.append(np.float32(v))
+        out_b.append(b)
+    return tuple(out_v), tuple(out_b)
 
 
 # ---------------------------------------------------------------- layout
