@@ -218,6 +218,7 @@ def run_llama8b(args):
 
     result["stream_read_ceiling"] = _stream_ceiling(kv, stream)
     result["decode"]["frac_of_stream_ceiling"] = round(decode_gbps / result["stream_read_ceiling"]["GBps"], 4)
+    result["calibrate"] = _calibrate(args, kv, K, V, T, row, ks, vs, stream)
     for h in handles:
         kv.kv_cache_free(h)
     handles = []
@@ -229,6 +230,33 @@ def run_llama8b(args):
         result["cpu_baseline"], result["parity_sample"] = _cpu_baseline(
             w, K, V, slots, q, out, ks, vs, args.cpu_seconds)
     return result
+
+
+def _calibrate(args, kv, K, V, T, row, ks, vs, stream):
+    """On-device scale calibration over the whole fill (K and V, 2 bytes per
+    element read): event time per call, and whether the fp32 scales it
+    produces equal the ones the input generator set for this workload."""
+    import torch
+    amax = torch.zeros(2, dtype=torch.float32, device=K.device)
+    out = torch.zeros(2, dtype=torch.int32, device=K.device)
+
+    def call(i):
+        kv.kv_calibrate_scales(K, V, row, row, T, row, amax, out, kv.DTYPE_F32, stream)
+
+    for i in range(args.warmup):
+        call(i)
+    ev = []
+    for i in range(args.steps):
+        _time_ms(lambda: call(i), stream, ev)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nbytes = 2 * T * row * 2 + 8 + 8
+    got = out.cpu().numpy().view(np.float32)
+    return {"ms_mean": round(ms, 5), "algorithmic_bytes": nbytes,
+            "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "scales_equal_generator": bool(got[0] == np.float32(ks) and got[1] == np.float32(vs)),
+            "kernel": "amax_kernel + scale_kernel"}
 
 
 def _typed_exchange(args, kv, w, K, V, slots_d, T, q, tables, lens, max_len, out, ks, vs, fp8_ms, stream):

@@ -46,6 +46,7 @@ SIGNATURES = {
     "paged_attn_prefill_chunk": (I32, [P, I32, P, I32, P, P, P, I32, I32, I64, I32, I32, F32, P,
                                        I32, P]),
     "kv_shift_rope": (I32, [P, I32, P, I64, I32, F32, I32, I32, P]),
+    "kv_calibrate_scales": (I32, [P, P, I64, I64, I64, I64, P, P, I32, P]),
     "kvf8_read_probe": (I32, [P, SZ, P, I32, P]),
 }
 
@@ -237,6 +238,13 @@ def kv_shift_rope(cache, layer: int, slots, n_slots: int, delta: int, theta_base
                   rot_dim: int, style: int, stream=None) -> None:
     _check(_lib.kv_shift_rope(cache, layer, _ptr(slots), n_slots, delta, theta_base, rot_dim, style,
                               _stream(stream)))
+
+
+def kv_calibrate_scales(k_bf16, v_bf16, k_tok_stride: int, v_tok_stride: int, num_tokens: int,
+                        row_elems: int, amax, scales_out=None, scale_dtype: int = DTYPE_F32,
+                        stream=None) -> None:
+    _check(_lib.kv_calibrate_scales(_ptr(k_bf16), _ptr(v_bf16), k_tok_stride, v_tok_stride, num_tokens,
+                                    row_elems, _ptr(amax), _ptr(scales_out), scale_dtype, _stream(stream)))
 
 
 def kvf8_read_probe(buf, nbytes: int, out_words, n_out: int, stream=None) -> None:

@@ -541,6 +541,47 @@ kvf8_status kv_shift_rope(kvf8_cache *c, int32_t layer, const int64_t *slots, in
     return ok();
 }
 
+kvf8_status kv_calibrate_scales(const uint16_t *k_bf16, const uint16_t *v_bf16, int64_t k_tok_stride,
+                                int64_t v_tok_stride, int64_t num_tokens, int64_t row_elems, float *amax,
+                                void *scales_out, kvf8_dtype scale_dtype, void *stream) {
+    if (!amax) return fail(KVF8_E_INVALID, "amax must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(amax) % 4) != 0) return fail(KVF8_E_INVALID, "amax must be 4-byte aligned");
+    if (num_tokens < 0) return fail(KVF8_E_INVALID, "num_tokens must be >= 0");
+    if (row_elems <= 0 || row_elems % 8 != 0 || row_elems > (int64_t(1) << 31))
+        return fail(KVF8_E_INVALID, "row_elems (%lld) must be a positive multiple of 8, at most 2^31",
+                    (long long)row_elems);
+    const uint16_t *xs[2] = {k_bf16, v_bf16};
+    const int64_t strides[2] = {k_tok_stride, v_tok_stride};
+    kvf8::CalibArgs a{};
+    int32_t sides = 0;
+    for (int t = 0; t < 2; ++t) {
+        a.x[t] = xs[t];
+        a.stride[t] = strides[t];
+        if (!xs[t]) continue;
+        if (strides[t] < row_elems || strides[t] % 8 != 0 || (reinterpret_cast<uintptr_t>(xs[t]) % 16) != 0)
+            return fail(KVF8_E_INVALID,
+                        "%s rows must be 16-byte aligned: pointer 16-byte aligned, stride (%lld) a multiple of 8 "
+                        "and >= row_elems (%lld)", t ? "V" : "K", (long long)strides[t], (long long)row_elems);
+        if (num_tokens > (int64_t(1) << 62) / strides[t])
+            return fail(KVF8_E_INVALID, "num_tokens * stride must stay below 2^62");
+        a.side[sides++] = t;
+    }
+    if (scales_out) {
+        if (scale_dtype != KVF8_DTYPE_F32 && scale_dtype != KVF8_DTYPE_BF16)
+            return fail(KVF8_E_INVALID, "scale_dtype must be KVF8_DTYPE_F32 or KVF8_DTYPE_BF16");
+        const uintptr_t al = scale_dtype == KVF8_DTYPE_F32 ? 4 : 2;
+        if ((reinterpret_cast<uintptr_t>(scales_out) % al) != 0)
+            return fail(KVF8_E_INVALID, "scales_out must be aligned to its element size");
+    }
+    a.rows = num_tokens;
+    a.runs_per_row = row_elems / 8;
+    a.amax = reinterpret_cast<uint32_t *>(amax);
+    hipError_t e = kvf8::launch_calibrate(a, num_tokens > 0 ? sides : 0, scales_out,
+                                          scale_dtype == KVF8_DTYPE_BF16 ? 1 : 0, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kv_calibrate_scales launch");
+    return ok();
+}
+
 kvf8_status kvf8_read_probe(const void *buf, size_t bytes, uint32_t *out_words, int32_t n_out, void *stream) {
     if (bytes == 0) return ok();
     if (!buf || !out_words) return fail(KVF8_E_INVALID, "buf and out_words must be non-NULL");

@@ -122,6 +122,21 @@ struct PrefillArgs {
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 // ---------------------------------------------------------------- read probe
+// ---------------------------------------------------------------- calibration
+struct CalibArgs {
+    const uint16_t *x[2];    // K, V bf16 rows (a side may be null when not launched)
+    int64_t stride[2];       // elements between rows
+    int32_t side[2];         // tensor of grid row y: side[y] in {0 (K), 1 (V)}
+    int64_t rows;            // tokens
+    int64_t runs_per_row;    // 16-byte runs (8 elements) per row
+    uint32_t *amax;          // [2] running maxima as fp32 bit patterns
+};
+constexpr int64_t kCalibWorkgroups = 1024;   // amax workgroups per launch, over both tensors
+// amax over the sides present (sides = 0, 1 or 2), then, when scales_out is
+// non-null, the two scales from the maxima (fp32 or bf16 bit patterns).
+hipError_t launch_calibrate(const CalibArgs &a, int32_t sides, void *scales_out, int32_t out_bf16,
+                            hipStream_t stream);
+
 hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int32_t n_out, hipStream_t stream);
 
 }  // namespace kvf8

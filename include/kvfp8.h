@@ -299,6 +299,40 @@ kvf8_status kv_shift_rope(kvf8_cache *cache, int32_t layer, const int64_t *slots
                           kvf8_rope style, void *stream);
 
 /*
+ * Per-tensor scale calibration on the device: a running absolute maximum of
+ * bf16 K and V tensors and the scales s = amax / 448, which put each
+ * tensor's largest magnitude on E4M3's largest finite value (the amax / 448
+ * rule of vllm.cpp PR #1641, whose "Unreached and owed" list leaves run-time
+ * calibration unbuilt; 448 from ggml_fp32_to_f8_e4m3, git.wylab.me
+ * osimons/ocp_fp8_kv).  The scales are meant for kv_cache_alloc /
+ * kv_cache_set_scales, which take host values: copy scales_out to the host
+ * once the stream has finished.
+ *
+ * k_bf16, v_bf16 (device): [num_tokens][row_elems] bf16 rows, row i at
+ *   element i * k_tok_stride (resp. v_tok_stride); either may be NULL, which
+ *   leaves that side's maximum unchanged.  Rows 16-byte aligned (pointer
+ *   16-byte aligned, stride a multiple of 8 and >= row_elems); row_elems a
+ *   positive multiple of 8, at most 2^31.
+ * amax (device, caller-owned, 4-byte aligned): float [2], the running K and
+ *   V maxima.  Start each at +0.0; every call raises amax[0] (amax[1]) to the
+ *   largest |x| of the K (V) rows it reads, so calls over parts of a tensor
+ *   accumulate.  A NaN element makes that maximum the quiet NaN 0x7FC00000
+ *   (it stays NaN); infinities count as the largest values.
+ * scales_out (device, may be NULL): [2] scales (K, V) from the maxima after
+ *   this call, as fp32 bit patterns (scale_dtype KVF8_DTYPE_F32: the
+ *   correctly rounded quotient amax / 448) or bf16 bit patterns
+ *   (KVF8_DTYPE_BF16: that fp32 value rounded to the nearest bf16, ties to
+ *   even).  A NaN maximum gives the quiet NaN.  A zero or infinite maximum
+ *   gives a scale of 0 or infinity, which kv_cache_alloc and
+ *   kv_cache_set_scales refuse with KVF8_E_SCALE.
+ * num_tokens == 0 only computes the scales.  Asynchronous on `stream`; calls
+ * that share an amax buffer must be ordered on one stream.
+ */
+kvf8_status kv_calibrate_scales(const uint16_t *k_bf16, const uint16_t *v_bf16, int64_t k_tok_stride,
+                                int64_t v_tok_stride, int64_t num_tokens, int64_t row_elems, float *amax,
+                                void *scales_out, kvf8_dtype scale_dtype, void *stream);
+
+/*
  * Measurement aid, not a step of the cache: a plain streaming read of `bytes`
  * of device memory at `buf` (16-byte aligned, bytes a multiple of 16), the
  * achievable read-bandwidth ceiling that the cache kernels are reported

@@ -298,3 +298,30 @@ def test_typed_pools_host_rules():
                 assert ei.value.status == kv.E_UNSUPPORTED
         finally:
             kv.kv_cache_free(c)
+
+
+def test_calibrate_host_checks():
+    """Scale calibration refuses missing or misaligned state, ragged rows and bad scale
+    types before launching anything."""
+    A, X = 1 << 30, 1 << 31            # stand-in device addresses (never dereferenced)
+    bad = [
+        dict(amax=None),
+        dict(amax=A + 2),
+        dict(num_tokens=-1),
+        dict(row_elems=0),
+        dict(row_elems=12),
+        dict(k=X + 8),                 # not 16-byte aligned
+        dict(k_stride=1020),           # below row_elems
+        dict(v_stride=1028),           # not a multiple of 8
+        dict(scales_out=A + 64, scale_dtype=5),
+        dict(scales_out=A + 66, scale_dtype=kv.DTYPE_F32),
+        dict(num_tokens=1 << 60),
+    ]
+    base = dict(k=X, v=X + (1 << 28), k_stride=1024, v_stride=1024, num_tokens=4, row_elems=1024,
+                amax=A, scales_out=None, scale_dtype=kv.DTYPE_F32)
+    for change in bad:
+        a = dict(base, **change)
+        with pytest.raises(kv.KvF8Error) as ei:
+            kv.kv_calibrate_scales(a["k"], a["v"], a["k_stride"], a["v_stride"], a["num_tokens"],
+                                   a["row_elems"], a["amax"], a["scales_out"], a["scale_dtype"], 0)
+        assert ei.value.status == kv.E_INVALID, change
