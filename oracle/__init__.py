@@ -17,6 +17,9 @@ Parity status of each function (what pins it is in ``tests/test_oracle_*``):
                               one-key and identical-key special cases)
   kshift                      pinned (complex rotation in NumPy, delta 0,
                               angle pins)
+  kshift_per_slot             pinned (one delta everywhere = kshift; each slot
+                              = kshift of that slot alone; NumPy complex
+                              rotation per slot)
   kv_bytes_per_block          pinned (exact halving)
   amax / calibrate_scales     pinned (torch's abs-max, planted maxima and NaN,
                               power-of-two amax, fp64-then-fp32 division,
@@ -92,6 +95,8 @@ def _load():
         "orc_kshift": (ctypes.c_int, [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, P, i64,
                                       ctypes.c_int, f32, ctypes.c_int, ctypes.c_int]),
         "orc_kv_bytes_per_block": (i64, [ctypes.c_int] * 4),
+        "orc_kshift_per_slot": (ctypes.c_int, [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, P, P, i64,
+                                               f32, ctypes.c_int, ctypes.c_int]),
         "orc_amax_bf16": (f32, [P, i64, i64, i64, f32]),
         "orc_scale_from_amax": (f32, [f32]),
         "orc_f32_to_bf16_rne": (ctypes.c_uint16, [f32]),
@@ -307,5 +312,20 @@ def kshift(k_pool, slots, *, Hkv: int, D: int, BS: int, delta: int, theta: float
     NB = k_pool.size // (Hkv * BS * D)
     rc = _load().orc_kshift(_ptr(k_pool), Hkv, D, BS, NB, _ptr(s), s.size, int(delta),
                             float(np.float32(theta)), rot_dim, 1 if neox else 0)
+    if rc != 0:
+        raise MemoryError("oracle scratch allocation failed")
+
+
+def kshift_per_slot(k_pool, slots, deltas, *, Hkv: int, D: int, BS: int, theta: float, rot_dim: int,
+                    neox: bool) -> None:
+    """kshift with its own position delta per slot (deltas[i] for slots[i]), in place."""
+    s = _c(slots, np.int64)
+    dl = _c(deltas, np.int32)
+    assert s.shape == dl.shape
+    assert k_pool.dtype == np.uint8 and k_pool.flags.c_contiguous
+    assert k_pool.size % (Hkv * BS * D) == 0
+    NB = k_pool.size // (Hkv * BS * D)
+    rc = _load().orc_kshift_per_slot(_ptr(k_pool), Hkv, D, BS, NB, _ptr(s), _ptr(dl), s.size,
+                                     float(np.float32(theta)), rot_dim, 1 if neox else 0)
     if rc != 0:
         raise MemoryError("oracle scratch allocation failed")

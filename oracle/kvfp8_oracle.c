@@ -435,6 +435,36 @@ void orc_rope_table(int rot_dim, int delta, float theta, float *cos_out, float *
     }
 }
 
+/* Rotate every rotary pair of one slot's K rows (all kv-heads) by the
+ * angles whose fp32 cos/sin are cs[p], sn[p]. */
+static void orc_kshift_slot(uint8_t *k_pool, int Hkv, int D, int BS, int64_t slot,
+                            const float *cs, const float *sn, int rot_dim, int style)
+{
+    const int64_t block = slot / BS;
+    const int t = (int)(slot % BS);
+    for (int h = 0; h < Hkv; ++h) {
+        const int64_t base = orc_tile_base(block, h, Hkv, BS, D);
+        for (int p = 0; p < rot_dim / 2; ++p) {
+            const int d0 = style == 1 ? p : 2 * p;
+            const int d1 = style == 1 ? p + rot_dim / 2 : 2 * p + 1;
+            uint8_t *c0 = &k_pool[base + orc_k_tile_offset(t, d0, BS, D)];
+            uint8_t *c1 = &k_pool[base + orc_k_tile_offset(t, d1, BS, D)];
+            const float x0 = orc_e4m3_decode(*c0);
+            const float x1 = orc_e4m3_decode(*c1);
+            if (isnan(x0) || isnan(x1)) {
+                *c0 = 0x7F;
+                *c1 = 0x7F;
+                continue;
+            }
+            const double c = cs[p], s = sn[p];
+            const double r0 = (double)x0 * c - (double)x1 * s;
+            const double r1 = (double)x0 * s + (double)x1 * c;
+            *c0 = orc_e4m3_encode((float)r0);
+            *c1 = orc_e4m3_encode((float)r1);
+        }
+    }
+}
+
 int orc_kshift(uint8_t *k_pool, int Hkv, int D, int BS, int64_t NB,
                const int64_t *slots, int64_t n_slots,
                int delta, float theta, int rot_dim, int style)
@@ -450,29 +480,39 @@ int orc_kshift(uint8_t *k_pool, int Hkv, int D, int BS, int64_t NB,
         const int64_t slot = slots[i];
         if (slot < 0 || slot >= NB * BS)
             continue;
-        const int64_t block = slot / BS;
-        const int t = (int)(slot % BS);
-        for (int h = 0; h < Hkv; ++h) {
-            const int64_t base = orc_tile_base(block, h, Hkv, BS, D);
-            for (int p = 0; p < rot_dim / 2; ++p) {
-                const int d0 = style == 1 ? p : 2 * p;
-                const int d1 = style == 1 ? p + rot_dim / 2 : 2 * p + 1;
-                uint8_t *c0 = &k_pool[base + orc_k_tile_offset(t, d0, BS, D)];
-                uint8_t *c1 = &k_pool[base + orc_k_tile_offset(t, d1, BS, D)];
-                const float x0 = orc_e4m3_decode(*c0);
-                const float x1 = orc_e4m3_decode(*c1);
-                if (isnan(x0) || isnan(x1)) {
-                    *c0 = 0x7F;
-                    *c1 = 0x7F;
-                    continue;
-                }
-                const double c = cs[p], s = sn[p];
-                const double r0 = (double)x0 * c - (double)x1 * s;
-                const double r1 = (double)x0 * s + (double)x1 * c;
-                *c0 = orc_e4m3_encode((float)r0);
-                *c1 = orc_e4m3_encode((float)r1);
-            }
+        orc_kshift_slot(k_pool, Hkv, D, BS, slot, cs, sn, rot_dim, style);
+    }
+    free(cs); free(sn);
+    return 0;
+}
+
+/* Per-slot deltas [P1, tests/test-fp8.cpp check_fp8_context_shift: the
+ * shift tensor holds one position offset per cache cell, so cells move by
+ * different amounts in one pass]: slot slots[i] turns by deltas[i], each
+ * exactly as orc_kshift would turn it alone.  The angle table is rebuilt
+ * whenever the delta changes from the previous slot's. */
+int orc_kshift_per_slot(uint8_t *k_pool, int Hkv, int D, int BS, int64_t NB,
+                        const int64_t *slots, const int32_t *deltas, int64_t n_slots,
+                        float theta, int rot_dim, int style)
+{
+    float *cs = (float *)malloc(sizeof(float) * (size_t)(rot_dim / 2 + 1));
+    float *sn = (float *)malloc(sizeof(float) * (size_t)(rot_dim / 2 + 1));
+    if (!cs || !sn) {
+        free(cs); free(sn);
+        return -1;
+    }
+    int have = 0;
+    int32_t current = 0;
+    for (int64_t i = 0; i < n_slots; ++i) {
+        const int64_t slot = slots[i];
+        if (slot < 0 || slot >= NB * BS)
+            continue;
+        if (!have || deltas[i] != current) {
+            current = deltas[i];
+            orc_rope_table(rot_dim, current, theta, cs, sn);
+            have = 1;
         }
+        orc_kshift_slot(k_pool, Hkv, D, BS, slot, cs, sn, rot_dim, style);
     }
     free(cs); free(sn);
     return 0;

@@ -131,3 +131,38 @@ def test_kshift_there_and_back_within_envelope(orc):
                 na = np.hypot(a[:half], a[half:])
                 err = np.hypot(b[:half] - a[:half], b[half:] - a[half:])
                 assert np.all(err <= 2 * (2 ** -4 * np.sqrt(2) * na * 1.07 + 2 ** -10 * 2))
+
+
+@pytest.mark.parametrize("neox", [True, False])
+def test_per_slot_deltas(orc, neox):
+    """Each slot turns by its own delta [P1, tests/test-fp8.cpp
+    check_fp8_context_shift: one shift value per cache cell]: one delta
+    everywhere equals kshift; distinct deltas equal the NumPy complex rotation
+    of each slot by its own delta, and equal kshift run on each slot alone;
+    skipped slots stay untouched."""
+    rng = np.random.default_rng(5 + neox)
+    NB, Hkv, BS, D, rot, theta = 6, 2, 16, 64, 64, 10000.0
+    pool = _random_pool(rng, NB, Hkv, BS, D)
+    slots = rng.permutation(NB * BS)[:40].astype(np.int64)
+    slots[3] = -1
+    slots[9] = NB * BS + 5
+    # one delta everywhere
+    a, b = pool.copy(), pool.copy()
+    orc.kshift(a, slots, Hkv=Hkv, D=D, BS=BS, delta=-3, theta=theta, rot_dim=rot, neox=neox)
+    orc.kshift_per_slot(b, slots, np.full(slots.shape, -3, np.int32), Hkv=Hkv, D=D, BS=BS, theta=theta,
+                        rot_dim=rot, neox=neox)
+    assert np.array_equal(a, b)
+    # distinct deltas, repeats not adjacent
+    deltas = rng.choice(np.array([-4096, -1, 0, 5, 77], np.int32), size=slots.shape)
+    got = pool.copy()
+    orc.kshift_per_slot(got, slots, deltas, Hkv=Hkv, D=D, BS=BS, theta=theta, rot_dim=rot, neox=neox)
+    want = pool.copy()
+    alone = pool.copy()
+    for sl, dl in zip(slots, deltas):
+        if 0 <= sl < NB * BS:
+            want = _expected(orc, want, [sl], Hkv, D, BS, int(dl), theta, rot, neox)
+        orc.kshift(alone, np.array([sl]), Hkv=Hkv, D=D, BS=BS, delta=int(dl), theta=theta, rot_dim=rot,
+                   neox=neox)
+    assert np.array_equal(got, want)
+    assert np.array_equal(got, alone)
+    assert not np.array_equal(got, pool)
