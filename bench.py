@@ -605,8 +605,18 @@ def run_longctx(args):
         kv.kv_shift_rope(handles[i % copies], 0, slots, nsl, w.spec.delta, w.spec.theta, w.D,
                          kv.ROPE_NEOX, stream)
 
+    # the same shift with a position delta per sequence (one table row each)
+    seq_deltas = np.array([w.spec.delta - 512 * b for b in range(w.B)], np.int32)
+    table = torch.from_numpy(kv.kv_rope_table(seq_deltas, w.spec.theta, w.D)).to(dev)
+    rows = torch.from_numpy(np.repeat(np.arange(w.B, dtype=np.int32), lens.astype(np.int64))).to(dev)
+
+    def shift_per_slot(i):
+        kv.kv_shift_rope_per_slot(handles[i % copies], 0, slots, rows, nsl, table, w.B, w.D, kv.ROPE_NEOX,
+                                  stream)
+
     de = _timed(decode, args.steps, args.warmup, stream)
     sh = _timed(shift, args.steps, args.warmup, stream)
+    sp = _timed(shift_per_slot, args.steps, args.warmup, stream)
     de_bytes = _decode_bytes(w, lens, 2)
     sh_bytes = nsl * (2 * w.Hkv * w.D + 8)
     de_gbps = de_bytes / (de.mean() * 1e-3) / 1e9
@@ -621,6 +631,11 @@ def run_longctx(args):
     res["kv_shift"] = dict(_stats(sh), algorithmic_bytes=sh_bytes, GBps=round(sh_gbps, 1),
                            frac_hbm_peak=round(sh_gbps / HBM_PEAK_GBPS, 4),
                            tokens_per_s=round(nsl / (sh.mean() * 1e-3), 1))
+    sp_bytes = sh_bytes + nsl * 4
+    sp_gbps = sp_bytes / (sp.mean() * 1e-3) / 1e9
+    res["kv_shift_per_slot"] = dict(_stats(sp), algorithmic_bytes=sp_bytes, GBps=round(sp_gbps, 1),
+                                    frac_hbm_peak=round(sp_gbps / HBM_PEAK_GBPS, 4), distinct_deltas=w.B,
+                                    tokens_per_s=round(nsl / (sp.mean() * 1e-3), 1))
     res["roofline"] = {"bound": "hbm", "achieved": round(de_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                        "frac": round(de_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                        "kernel": "decode_kernel<256,32,1,1> + decode_reduce<256>"}

@@ -46,6 +46,8 @@ SIGNATURES = {
     "paged_attn_prefill_chunk": (I32, [P, I32, P, I32, P, P, P, I32, I32, I64, I32, I32, F32, P,
                                        I32, P]),
     "kv_shift_rope": (I32, [P, I32, P, I64, I32, F32, I32, I32, P]),
+    "kv_rope_table": (I32, [P, I32, F32, I32, P]),
+    "kv_shift_rope_per_slot": (I32, [P, I32, P, P, I64, P, I32, I32, I32, P]),
     "kv_calibrate_scales": (I32, [P, P, I64, I64, I64, I64, P, P, I32, P]),
     "kvf8_read_probe": (I32, [P, SZ, P, I32, P]),
 }
@@ -238,6 +240,22 @@ def kv_shift_rope(cache, layer: int, slots, n_slots: int, delta: int, theta_base
                   rot_dim: int, style: int, stream=None) -> None:
     _check(_lib.kv_shift_rope(cache, layer, _ptr(slots), n_slots, delta, theta_base, rot_dim, style,
                               _stream(stream)))
+
+
+def kv_rope_table(deltas, theta_base: float, rot_dim: int):
+    """Host cos/sin table [n_deltas][rot_dim/2][2] (numpy float32) for kv_shift_rope_per_slot."""
+    import numpy as np
+    d = np.ascontiguousarray(np.asarray(deltas, dtype=np.int32).reshape(-1))
+    table = np.zeros((d.size, rot_dim // 2, 2), np.float32)
+    _check(_lib.kv_rope_table(d.ctypes.data if d.size else None, d.size, theta_base, rot_dim,
+                              table.ctypes.data if d.size else None))
+    return table
+
+
+def kv_shift_rope_per_slot(cache, layer: int, slots, table_rows, n_slots: int, table, n_rows: int,
+                           rot_dim: int, style: int, stream=None) -> None:
+    _check(_lib.kv_shift_rope_per_slot(cache, layer, _ptr(slots), _ptr(table_rows), n_slots, _ptr(table),
+                                       n_rows, rot_dim, style, _stream(stream)))
 
 
 def kv_calibrate_scales(k_bf16, v_bf16, k_tok_stride: int, v_tok_stride: int, num_tokens: int,

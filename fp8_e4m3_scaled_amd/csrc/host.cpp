@@ -503,12 +503,19 @@ kvf8_status paged_attn_prefill_chunk(kvf8_cache *c, int32_t layer, const uint16_
     return ok();
 }
 
-kvf8_status kv_shift_rope(kvf8_cache *c, int32_t layer, const int64_t *slots, int64_t n_slots,
-                          int32_t delta, float theta_base, int32_t rot_dim, kvf8_rope style,
-                          void *stream) {
-    kvf8_status st = check_layer(c, layer);
-    if (st != KVF8_OK) return st;
-    if (n_slots < 0) return fail(KVF8_E_INVALID, "n_slots must be >= 0");
+}  // extern "C"
+
+namespace {
+// Angle of rotary pair i for a position delta: a_i = delta * theta^(-2i/rot),
+// cos/sin in double rounded to fp32 (the contract stated in kvfp8.h).
+void rope_angle(int32_t delta, float theta_base, int32_t rot_dim, int32_t i, float &c, float &s) {
+    const double omega = std::pow((double)theta_base, -2.0 * (double)i / (double)rot_dim);
+    const double ang = (double)delta * omega;
+    c = (float)std::cos(ang);
+    s = (float)std::sin(ang);
+}
+
+kvf8_status check_rope(const kvf8_cache *c, float theta_base, int32_t rot_dim, kvf8_rope style) {
     if (rot_dim < 2 || (rot_dim % 2) != 0 || rot_dim > c->head_dim)
         return fail(KVF8_E_INVALID, "rot_dim %d must be even and in [2, head_dim=%d]", rot_dim, c->head_dim);
     if (!(std::isfinite(theta_base) && theta_base > 0.0f))
@@ -516,6 +523,20 @@ kvf8_status kv_shift_rope(kvf8_cache *c, int32_t layer, const int64_t *slots, in
     if (style != KVF8_ROPE_NORM && style != KVF8_ROPE_NEOX)
         return fail(KVF8_E_INVALID, "style must be KVF8_ROPE_NORM or KVF8_ROPE_NEOX");
     if (c->k_eb != 1) return fail(KVF8_E_UNSUPPORTED, "kv_shift_rope needs an E4M3 K pool");
+    return KVF8_OK;
+}
+}  // namespace
+
+extern "C" {
+
+kvf8_status kv_shift_rope(kvf8_cache *c, int32_t layer, const int64_t *slots, int64_t n_slots,
+                          int32_t delta, float theta_base, int32_t rot_dim, kvf8_rope style,
+                          void *stream) {
+    kvf8_status st = check_layer(c, layer);
+    if (st != KVF8_OK) return st;
+    if (n_slots < 0) return fail(KVF8_E_INVALID, "n_slots must be >= 0");
+    st = check_rope(c, theta_base, rot_dim, style);
+    if (st != KVF8_OK) return st;
     if (n_slots == 0) return ok();
     if (!slots) return fail(KVF8_E_INVALID, "slots is NULL");
     kvf8::KShiftArgs a{};
@@ -528,16 +549,56 @@ kvf8_status kv_shift_rope(kvf8_cache *c, int32_t layer, const int64_t *slots, in
     a.block_size = c->block_size;
     a.rot_dim = rot_dim;
     a.neox = style == KVF8_ROPE_NEOX;
-    // Angle table on the host: a_i = delta * theta^(-2i/rot), cos/sin in
-    // double rounded to fp32 (the contract stated in kvfp8.h).
-    for (int32_t i = 0; i < rot_dim / 2; ++i) {
-        const double omega = std::pow((double)theta_base, -2.0 * (double)i / (double)rot_dim);
-        const double ang = (double)delta * omega;
-        a.cos_t[i] = (float)std::cos(ang);
-        a.sin_t[i] = (float)std::sin(ang);
-    }
+    for (int32_t i = 0; i < rot_dim / 2; ++i) rope_angle(delta, theta_base, rot_dim, i, a.cos_t[i], a.sin_t[i]);
     hipError_t e = kvf8::launch_kshift(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "kv_shift_rope launch");
+    return ok();
+}
+
+kvf8_status kv_rope_table(const int32_t *deltas, int32_t n_deltas, float theta_base, int32_t rot_dim,
+                          float *table) {
+    if (n_deltas < 0) return fail(KVF8_E_INVALID, "n_deltas must be >= 0");
+    if (rot_dim < 2 || (rot_dim % 2) != 0 || rot_dim > 256)
+        return fail(KVF8_E_INVALID, "rot_dim %d must be even and in [2, 256]", rot_dim);
+    if (!(std::isfinite(theta_base) && theta_base > 0.0f))
+        return fail(KVF8_E_INVALID, "theta_base must be finite and > 0");
+    if (n_deltas == 0) return ok();
+    if (!deltas || !table) return fail(KVF8_E_INVALID, "deltas and table must be non-NULL");
+    const int32_t half = rot_dim / 2;
+    for (int32_t j = 0; j < n_deltas; ++j)
+        for (int32_t i = 0; i < half; ++i)
+            rope_angle(deltas[j], theta_base, rot_dim, i, table[((int64_t)j * half + i) * 2],
+                       table[((int64_t)j * half + i) * 2 + 1]);
+    return ok();
+}
+
+kvf8_status kv_shift_rope_per_slot(kvf8_cache *c, int32_t layer, const int64_t *slots, const int32_t *table_rows,
+                                   int64_t n_slots, const float *table, int32_t n_rows, int32_t rot_dim,
+                                   kvf8_rope style, void *stream) {
+    kvf8_status st = check_layer(c, layer);
+    if (st != KVF8_OK) return st;
+    if (n_slots < 0) return fail(KVF8_E_INVALID, "n_slots must be >= 0");
+    st = check_rope(c, 1.0f, rot_dim, style);
+    if (st != KVF8_OK) return st;
+    if (n_rows < 1) return fail(KVF8_E_INVALID, "n_rows must be >= 1");
+    if (n_slots == 0) return ok();
+    if (!slots || !table_rows || !table) return fail(KVF8_E_INVALID, "slots, table_rows and table must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(table) % 16) != 0) return fail(KVF8_E_INVALID, "table must be 16-byte aligned");
+    kvf8::KShiftArgs a{};
+    a.k_pool = k_pool_of(c, layer);
+    a.slots = slots;
+    a.n_slots = n_slots;
+    a.pool_slots = c->num_blocks * c->block_size;
+    a.kv_heads = c->kv_heads;
+    a.head_dim = c->head_dim;
+    a.block_size = c->block_size;
+    a.rot_dim = rot_dim;
+    a.neox = style == KVF8_ROPE_NEOX;
+    a.rows = table_rows;
+    a.table = table;
+    a.n_rows = n_rows;
+    hipError_t e = kvf8::launch_kshift(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kv_shift_rope_per_slot launch");
     return ok();
 }
 

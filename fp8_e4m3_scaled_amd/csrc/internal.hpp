@@ -92,8 +92,11 @@ struct KShiftArgs {
     int32_t block_size;
     int32_t rot_dim;
     int32_t neox;
-    float cos_t[128];
+    float cos_t[128];        // one delta for every slot (rows == nullptr) ...
     float sin_t[128];
+    const int32_t *rows;     // ... or a row of `table` per slot: [n_rows][rot_dim/2][cos, sin]
+    const float *table;
+    int32_t n_rows;
 };
 hipError_t launch_kshift(const KShiftArgs &a, hipStream_t stream);
 

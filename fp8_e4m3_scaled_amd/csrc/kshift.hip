@@ -17,6 +17,12 @@
 // row (both inside a column quarter of the tile, hence contiguous): NEOX runs
 // [16r, 16r+16) and [16r + rot/2, ...); NORM one run [16r, 16r+16) holding
 // eight (2i, 2i+1) pairs.  Byte path (any other even rot): one pair per thread.
+//
+// Per-slot deltas (kv_shift_rope_per_slot): each slot names a row of a cos/sin
+// table in device memory, built on the host for each distinct delta exactly
+// as the single-delta table; the same rotation then runs with that row's
+// values.  [P1, tests/test-fp8.cpp check_fp8_context_shift: the shift tensor
+// holds one offset per cache cell.]
 
 #include "fp8_device.hpp"
 #include "internal.hpp"
@@ -64,6 +70,52 @@ __device__ __forceinline__ void rotate_finite(float x0, float x1, double c, doub
     const double a = (double)x0, b = (double)x1;
     y0 = (float)__builtin_fma(a, c, -(b * s));
     y1 = (float)__builtin_fma(a, s, b * c);
+}
+
+// Rotate the pairs held in one run (NORM: eight (2i, 2i+1) pairs in A) or two
+// runs (NEOX: A holds dims of the first half, B the partners) with cos/sin in
+// cs/sn; na/nb receive the new codes.
+template <bool NEOX, int NP>
+__device__ __forceinline__ void rotate_runs(const u32x4 &wa, const u32x4 &wb, const double (&cs)[NP],
+                                            const double (&sn)[NP], u32x4 &na, u32x4 &nb) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t A = wa[w], B = NEOX ? wb[w] : 0u;
+        const f32x2 a01 = codes_to_f32x2<false>(A), a23 = codes_to_f32x2<true>(A);
+        if (NEOX) {
+            const f32x2 b01 = codes_to_f32x2<false>(B), b23 = codes_to_f32x2<true>(B);
+            const float xa[4] = {a01[0], a01[1], a23[0], a23[1]};
+            const float xb[4] = {b01[0], b01[1], b23[0], b23[1]};
+            if (!(has_nan4(A) || has_nan4(B))) {
+                float y0[4], y1[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) rotate_finite(xa[k], xb[k], cs[4 * w + k], sn[4 * w + k], y0[k], y1[k]);
+                na[w] = encode4_finite(y0[0], y0[1], y0[2], y0[3]);
+                nb[w] = encode4_finite(y1[0], y1[1], y1[2], y1[3]);
+            } else {
+                uint32_t ca = 0, cb = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t y = rotate_pair(xa[k], xb[k], cs[4 * w + k], sn[4 * w + k]);
+                    ca |= (y & 0xFFu) << (8 * k);
+                    cb |= ((y >> 8) & 0xFFu) << (8 * k);
+                }
+                na[w] = ca;
+                nb[w] = cb;
+            }
+        } else {
+            if (!has_nan4(A)) {
+                float p0, q0, p1, q1;
+                rotate_finite(a01[0], a01[1], cs[2 * w], sn[2 * w], p0, q0);
+                rotate_finite(a23[0], a23[1], cs[2 * w + 1], sn[2 * w + 1], p1, q1);
+                na[w] = encode4_finite(p0, q0, p1, q1);
+            } else {
+                const uint32_t y0 = rotate_pair(a01[0], a01[1], cs[2 * w], sn[2 * w]);
+                const uint32_t y1 = rotate_pair(a23[0], a23[1], cs[2 * w + 1], sn[2 * w + 1]);
+                na[w] = (y0 & 0xFFFFu) | (y1 << 16);
+            }
+        }
+    }
 }
 
 // Run path.  Thread g works on run r = g mod RP (RP: runs per row rounded up to
@@ -133,49 +185,100 @@ __global__ __launch_bounds__(kThreads) void kshift_runs(KShiftArgs a, int rp_log
         for (int u = 0; u < U; ++u) {
             if (oa[u] < 0) continue;
             u32x4 na, nb;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t A = wa[u][w], B = NEOX ? wb[u][w] : 0u;
-                const f32x2 a01 = codes_to_f32x2<false>(A), a23 = codes_to_f32x2<true>(A);
-                if (NEOX) {
-                    const f32x2 b01 = codes_to_f32x2<false>(B), b23 = codes_to_f32x2<true>(B);
-                    const float xa[4] = {a01[0], a01[1], a23[0], a23[1]};
-                    const float xb[4] = {b01[0], b01[1], b23[0], b23[1]};
-                    if (!(has_nan4(A) || has_nan4(B))) {
-                        float y0[4], y1[4];
-#pragma unroll
-                        for (int k = 0; k < 4; ++k)
-                            rotate_finite(xa[k], xb[k], cs[4 * w + k], sn[4 * w + k], y0[k], y1[k]);
-                        na[w] = encode4_finite(y0[0], y0[1], y0[2], y0[3]);
-                        nb[w] = encode4_finite(y1[0], y1[1], y1[2], y1[3]);
-                    } else {
-                        uint32_t ca = 0, cb = 0;
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) {
-                            const uint32_t y = rotate_pair(xa[k], xb[k], cs[4 * w + k], sn[4 * w + k]);
-                            ca |= (y & 0xFFu) << (8 * k);
-                            cb |= ((y >> 8) & 0xFFu) << (8 * k);
-                        }
-                        na[w] = ca;
-                        nb[w] = cb;
-                    }
-                } else {
-                    if (!has_nan4(A)) {
-                        float p0, q0, p1, q1;
-                        rotate_finite(a01[0], a01[1], cs[2 * w], sn[2 * w], p0, q0);
-                        rotate_finite(a23[0], a23[1], cs[2 * w + 1], sn[2 * w + 1], p1, q1);
-                        na[w] = encode4_finite(p0, q0, p1, q1);
-                    } else {
-                        const uint32_t y0 = rotate_pair(a01[0], a01[1], cs[2 * w], sn[2 * w]);
-                        const uint32_t y1 = rotate_pair(a23[0], a23[1], cs[2 * w + 1], sn[2 * w + 1]);
-                        na[w] = (y0 & 0xFFFFu) | (y1 << 16);
-                    }
-                }
-            }
+            rotate_runs<NEOX, NP>(wa[u], wb[u], cs, sn, na, nb);
             *reinterpret_cast<u32x4 *>(a.k_pool + oa[u]) = na;
             if (NEOX) *reinterpret_cast<u32x4 *>(a.k_pool + ob[u]) = nb;
         }
     }
+}
+
+// Per-slot path, runs.  Every slot carries its own row of the cos/sin table
+// (a.rows[si] into a.table, [row][pair][cos, sin] fp32).  Thread g works on
+// run r = g mod RP of slots g / RP, g / RP + J, ...; for each slot it loads its
+// run's cos/sin once (16-byte loads of the interleaved row) and rotates that
+// run in every kv-head, two heads in flight.
+template <bool NEOX>
+__global__ __launch_bounds__(kThreads) void kshift_slot_runs(KShiftArgs a, int rp_log2) {
+    constexpr int NP = NEOX ? 16 : 8;
+    const int D = a.head_dim, H = a.kv_heads;
+    const int bs_log2 = a.block_size == 32 ? 5 : 4;
+    const int runs = NEOX ? a.rot_dim / 32 : a.rot_dim / 16;
+    const int half = a.rot_dim / 2;
+    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int r = (int)(g & ((1 << rp_log2) - 1));
+    if (r >= runs) return;
+    const int64_t sstep = ((int64_t)gridDim.x * kThreads) >> rp_log2;
+    const int p0 = NEOX ? 16 * r : 8 * r;
+    const int da = 16 * r;
+    const int db = da + half;
+    for (int64_t si = g >> rp_log2; si < a.n_slots; si += sstep) {
+        const int64_t slot = a.slots[si];
+        const int32_t row = a.rows[si];
+        if (slot < 0 || slot >= a.pool_slots || row < 0 || row >= a.n_rows) continue;
+        const f32x4 *tp = reinterpret_cast<const f32x4 *>(a.table + ((int64_t)row * half + p0) * 2);
+        double cs[NP], sn[NP];
+#pragma unroll
+        for (int k = 0; k < NP / 2; ++k) {
+            const f32x4 v = tp[k];
+            cs[2 * k] = (double)v[0];
+            sn[2 * k] = (double)v[1];
+            cs[2 * k + 1] = (double)v[2];
+            sn[2 * k + 1] = (double)v[3];
+        }
+        const int64_t blk = slot >> bs_log2;
+        const int t = (int)(slot - (blk << bs_log2));
+        const int64_t oa0 = k_offset(t, da, a.block_size, D), ob0 = k_offset(t, db, a.block_size, D);
+        const int64_t head_bytes = ((int64_t)1 << bs_log2) * D;
+        uint8_t *base = a.k_pool + blk * H * head_bytes;
+        for (int h = 0; h < H; h += 2) {
+            const bool two = h + 1 < H;
+            uint8_t *t0 = base + h * head_bytes;
+            uint8_t *t1 = t0 + head_bytes;
+            u32x4 wa0, wb0 = {0u, 0u, 0u, 0u}, wa1 = {0u, 0u, 0u, 0u}, wb1 = {0u, 0u, 0u, 0u};
+            wa0 = *reinterpret_cast<const u32x4 *>(t0 + oa0);
+            if (NEOX) wb0 = *reinterpret_cast<const u32x4 *>(t0 + ob0);
+            if (two) {
+                wa1 = *reinterpret_cast<const u32x4 *>(t1 + oa0);
+                if (NEOX) wb1 = *reinterpret_cast<const u32x4 *>(t1 + ob0);
+            }
+            u32x4 na, nb;
+            rotate_runs<NEOX, NP>(wa0, wb0, cs, sn, na, nb);
+            *reinterpret_cast<u32x4 *>(t0 + oa0) = na;
+            if (NEOX) *reinterpret_cast<u32x4 *>(t0 + ob0) = nb;
+            if (two) {
+                rotate_runs<NEOX, NP>(wa1, wb1, cs, sn, na, nb);
+                *reinterpret_cast<u32x4 *>(t1 + oa0) = na;
+                if (NEOX) *reinterpret_cast<u32x4 *>(t1 + ob0) = nb;
+            }
+        }
+    }
+}
+
+// Per-slot path, one pair per thread (rotary widths the run path does not cover).
+__global__ __launch_bounds__(kThreads) void kshift_slot_pairs(KShiftArgs a) {
+    const int D = a.head_dim, BS = a.block_size, H = a.kv_heads;
+    const int half = a.rot_dim / 2;
+    const int64_t item = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t total = a.n_slots * H * half;
+    if (item >= total) return;
+    const int p = (int)(item % half);
+    const int h = (int)((item / half) % H);
+    const int64_t si = item / ((int64_t)half * H);
+    const int64_t slot = a.slots[si];
+    const int32_t row = a.rows[si];
+    if (slot < 0 || slot >= a.pool_slots || row < 0 || row >= a.n_rows) return;
+    const f32x2 cs = *reinterpret_cast<const f32x2 *>(a.table + ((int64_t)row * half + p) * 2);
+    const int64_t blk = slot / BS;
+    const int t = (int)(slot - blk * BS);
+    uint8_t *tile = a.k_pool + (blk * H + h) * (int64_t)BS * D;
+    const int d0 = a.neox ? p : 2 * p;
+    const int d1 = a.neox ? p + half : 2 * p + 1;
+    uint8_t *b0 = tile + k_offset(t, d0, BS, D);
+    uint8_t *b1 = tile + k_offset(t, d1, BS, D);
+    const f32x2 x = codes_to_f32x2<false>((uint32_t)*b0 | ((uint32_t)*b1 << 8));
+    const uint32_t y = rotate_pair(x[0], x[1], (double)cs[0], (double)cs[1]);
+    *b0 = (uint8_t)(y & 0xFF);
+    *b1 = (uint8_t)(y >> 8);
 }
 
 __global__ __launch_bounds__(kThreads) void kshift_pairs(KShiftArgs a) {
@@ -208,6 +311,28 @@ __global__ __launch_bounds__(kThreads) void kshift_pairs(KShiftArgs a) {
 
 hipError_t launch_kshift(const KShiftArgs &a, hipStream_t stream) {
     const bool runs = a.neox ? (a.rot_dim % 32 == 0) : (a.rot_dim % 16 == 0);
+    if (a.rows) {
+        if (runs) {
+            const int per_row = a.neox ? a.rot_dim / 32 : a.rot_dim / 16;
+            int rp_log2 = 0;
+            while ((1 << rp_log2) < per_row) ++rp_log2;
+            int64_t wgs = ((a.n_slots << rp_log2) + kThreads - 1) / kThreads;
+            if (wgs > kRunsMaxWgs) wgs = kRunsMaxWgs;
+            if (wgs < 1) wgs = 1;
+            if (a.neox)
+                hipLaunchKernelGGL(kshift_slot_runs<true>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a,
+                                   rp_log2);
+            else
+                hipLaunchKernelGGL(kshift_slot_runs<false>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a,
+                                   rp_log2);
+            return hipGetLastError();
+        }
+        const int64_t total = a.n_slots * a.kv_heads * (a.rot_dim / 2);
+        const int64_t wgs = (total + kThreads - 1) / kThreads;
+        if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(kshift_slot_pairs, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+        return hipGetLastError();
+    }
     if (runs) {
         const int per_row = a.neox ? a.rot_dim / 32 : a.rot_dim / 16;
         int rp_log2 = 0;

@@ -299,6 +299,33 @@ kvf8_status kv_shift_rope(kvf8_cache *cache, int32_t layer, const int64_t *slots
                           kvf8_rope style, void *stream);
 
 /*
+ * Position deltas per slot [P1, tests/test-fp8.cpp check_fp8_context_shift:
+ * the shift tensor holds one offset per cache cell, so one pass moves cells
+ * by different amounts].  Two calls:
+ *
+ * kv_rope_table (host only): table[j][i] = (cos a, sin a) as fp32, with
+ *   a = deltas[j] * theta_base^(-2i/rot_dim) for 0 <= i < rot_dim/2, the
+ *   same values kv_shift_rope computes for a single delta.  deltas: host
+ *   int32 [n_deltas]; table: host float [n_deltas][rot_dim/2][2],
+ *   caller-owned.  rot_dim even in [2, 256]; theta_base finite and > 0.
+ *
+ * kv_shift_rope_per_slot: slot slots[k] turns by the angles of table row
+ *   table_rows[k], exactly as kv_shift_rope turns it for that row's delta.
+ *   slots (device): int64 [n_slots], no repeats; negative slots, slots at or
+ *   past num_blocks * block_size, and rows outside [0, n_rows) are skipped.
+ *   table_rows (device): int32 [n_slots].  table (device, 16-byte aligned,
+ *   caller-owned): the kv_rope_table output for n_rows deltas, copied to the
+ *   device.  rot_dim and style as in kv_shift_rope (the table must have been
+ *   built for the same rot_dim).  Asynchronous on `stream`; an E4M3 K pool
+ *   only (KVF8_E_UNSUPPORTED otherwise).
+ */
+kvf8_status kv_rope_table(const int32_t *deltas, int32_t n_deltas, float theta_base, int32_t rot_dim,
+                          float *table);
+kvf8_status kv_shift_rope_per_slot(kvf8_cache *cache, int32_t layer, const int64_t *slots,
+                                   const int32_t *table_rows, int64_t n_slots, const float *table,
+                                   int32_t n_rows, int32_t rot_dim, kvf8_rope style, void *stream);
+
+/*
  * Per-tensor scale calibration on the device: a running absolute maximum of
  * bf16 K and V tensors and the scales s = amax / 448, which put each
  * tensor's largest magnitude on E4M3's largest finite value (the amax / 448

@@ -325,3 +325,48 @@ def test_calibrate_host_checks():
             kv.kv_calibrate_scales(a["k"], a["v"], a["k_stride"], a["v_stride"], a["num_tokens"],
                                    a["row_elems"], a["amax"], a["scales_out"], a["scale_dtype"], 0)
         assert ei.value.status == kv.E_INVALID, change
+
+
+def test_rope_table_equals_oracle_table():
+    """The host cos/sin table behind the per-slot K-shift holds, for every delta,
+    the same fp32 values as the oracle's own angle table (both take cos/sin of
+    delta * theta^(-2i/rot) in double and round to fp32)."""
+    import numpy as np
+    import oracle
+    deltas = [-131072, -4096, -1, 0, 1, 3, 17, 4096, 100000, 2 ** 31 - 1]
+    for rot, theta in ((256, 1e6), (128, 5e5), (64, 1e4), (40, 1e4), (2, 1e4)):
+        t = kv.kv_rope_table(deltas, theta, rot)
+        assert t.shape == (len(deltas), rot // 2, 2)
+        for j, d in enumerate(deltas):
+            c, s = oracle.rope_table(rot, d, theta)
+            assert np.array_equal(t[j, :, 0].view(np.uint32), c.view(np.uint32)), (rot, d)
+            assert np.array_equal(t[j, :, 1].view(np.uint32), s.view(np.uint32)), (rot, d)
+    assert kv.kv_rope_table([], 1e4, 64).shape == (0, 32, 2)
+    for rot, theta in ((0, 1e4), (3, 1e4), (258, 1e4), (64, 0.0), (64, float("inf"))):
+        with pytest.raises(kv.KvF8Error) as ei:
+            kv.kv_rope_table([1], theta, rot)
+        assert ei.value.status == kv.E_INVALID
+
+
+def test_per_slot_shift_host_checks():
+    """kv_shift_rope_per_slot validates before launching: rot_dim, style, table
+    rows, pointers and table alignment; an empty slot list is a no-op."""
+    h = kv.kv_cache_alloc(1, 8, 16, 2, 64, [0.5], [0.5], kv.DTYPE_F32, FAKE_K, FAKE_V)
+    try:
+        T, S, R = 1 << 33, 1 << 34, 1 << 35
+        kv.kv_shift_rope_per_slot(h, 0, None, None, 0, None, 1, 64, kv.ROPE_NEOX, 0)
+        for args in [(h, 1, S, R, 4, T, 1, 64, kv.ROPE_NEOX),          # layer
+                     (h, 0, S, R, -1, T, 1, 64, kv.ROPE_NEOX),         # n_slots
+                     (h, 0, S, R, 4, T, 1, 66, kv.ROPE_NEOX),          # rot_dim > head_dim
+                     (h, 0, S, R, 4, T, 1, 63, kv.ROPE_NEOX),          # odd rot_dim
+                     (h, 0, S, R, 4, T, 1, 64, 9),                     # style
+                     (h, 0, S, R, 4, T, 0, 64, kv.ROPE_NEOX),          # n_rows
+                     (h, 0, None, R, 4, T, 1, 64, kv.ROPE_NEOX),
+                     (h, 0, S, None, 4, T, 1, 64, kv.ROPE_NEOX),
+                     (h, 0, S, R, 4, None, 1, 64, kv.ROPE_NEOX),
+                     (h, 0, S, R, 4, T + 8, 1, 64, kv.ROPE_NEOX)]:     # table alignment
+            with pytest.raises(kv.KvF8Error) as ei:
+                kv.kv_shift_rope_per_slot(*args, 0)
+            assert ei.value.status == kv.E_INVALID, args
+    finally:
+        kv.kv_cache_free(h)
