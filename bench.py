@@ -218,6 +218,10 @@ def run_llama8b(args):
 
     result["stream_read_ceiling"] = _stream_ceiling(kv, stream)
     result["decode"]["frac_of_stream_ceiling"] = round(decode_gbps / result["stream_read_ceiling"]["GBps"], 4)
+    result["paged_gather_ceiling"] = _gather_ceiling(args, kv, handles, tables, w.max_blocks, lens, w.B, w.Hkv,
+                                                     kv_bytes, stream)
+    result["decode"]["frac_of_gather_ceiling"] = round(
+        decode_gbps / result["paged_gather_ceiling"]["GBps"], 4)
     result["calibrate"] = _calibrate(args, kv, K, V, T, row, ks, vs, stream)
     for h in handles:
         kv.kv_cache_free(h)
@@ -311,6 +315,29 @@ def _typed_exchange(args, kv, w, K, V, slots_d, T, q, tables, lens, max_len, out
         del pools, ws
         torch.cuda.empty_cache()
     return res
+
+
+def _gather_ceiling(args, kv, handles, tables, max_blocks, lens, B, Hkv, kv_bytes, stream):
+    """kvf8_gather_probe over the decode's own pools and block tables: a plain
+    read of exactly the K/V tiles the decode reads, the ceiling of its
+    scattered-tile access pattern.  GB/s counts the K/V bytes only."""
+    import torch
+    out = torch.empty(B * Hkv, dtype=torch.int32, device="cuda")
+    copies = len(handles)
+
+    def call(i):
+        kv.kvf8_gather_probe(handles[(i + 1) % copies], 0, tables, max_blocks, lens, B, out, stream)
+
+    for i in range(args.warmup):
+        call(i)
+    ev = []
+    for i in range(args.steps):
+        _time_ms(lambda: call(i), stream, ev)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    gbps = kv_bytes / (ms * 1e-3) / 1e9
+    return {"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "ms_mean": round(ms, 5),
+            "bytes": kv_bytes, "kernel": "kvf8_gather_probe (one workgroup per (sequence, kv-head))"}
 
 
 def _stream_ceiling(kv, stream, nbytes=2 << 30, launches=20):

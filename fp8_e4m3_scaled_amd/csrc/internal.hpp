@@ -142,4 +142,19 @@ hipError_t launch_calibrate(const CalibArgs &a, int32_t sides, void *scales_out,
 
 hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int32_t n_out, hipStream_t stream);
 
+struct GatherProbeArgs {
+    const uint8_t *k_pool;   // this layer
+    const uint8_t *v_pool;
+    const int32_t *block_tables;
+    const int32_t *seq_lens;
+    uint32_t *out;           // [num_seqs * kv_heads]
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t kv_heads;
+    int32_t block_size;
+    int32_t k_words_log2;    // log2 of 16-byte words per (block, kv-head) tile
+    int32_t v_words_log2;
+};
+hipError_t launch_gather_probe(const GatherProbeArgs &a, hipStream_t stream);
+
 }  // namespace kvf8

@@ -370,3 +370,17 @@ def test_per_slot_shift_host_checks():
             assert ei.value.status == kv.E_INVALID, args
     finally:
         kv.kv_cache_free(h)
+
+
+def test_gather_probe_host_checks():
+    h = kv.kv_cache_alloc(1, 8, 16, 2, 64, [0.5], [0.5], kv.DTYPE_F32, FAKE_K, FAKE_V)
+    try:
+        kv.kvf8_gather_probe(h, 0, None, 4, None, 0, None, 0)          # no sequences: no-op
+        for args in [(h, 1, 1 << 33, 4, 1 << 34, 2, 1 << 35), (h, 0, 1 << 33, -1, 1 << 34, 2, 1 << 35),
+                     (h, 0, None, 4, 1 << 34, 2, 1 << 35), (h, 0, 1 << 33, 4, None, 2, 1 << 35),
+                     (h, 0, 1 << 33, 4, 1 << 34, 2, None), (h, 0, 1 << 33, 4, 1 << 34, -1, 1 << 35)]:
+            with pytest.raises(kv.KvF8Error) as ei:
+                kv.kvf8_gather_probe(*args, 0)
+            assert ei.value.status == kv.E_INVALID, args
+    finally:
+        kv.kv_cache_free(h)

@@ -24,3 +24,40 @@ def test_read_probe_xor(nbytes, n_out):
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
     assert int(got) == int(np.bitwise_xor.reduce(host))
+
+
+@pytest.mark.parametrize("BS,Hkv,D,v_elem", [(16, 2, 64, kv.ELEM_E4M3), (32, 3, 256, kv.ELEM_E4M3),
+                                              (16, 8, 128, kv.ELEM_BF16)])
+def test_gather_probe_xor(BS, Hkv, D, v_elem):
+    """The paged-gather measurement read covers exactly the decode's tiles: per
+    (sequence, kv-head), the XOR of every word of the K and V tiles of the
+    sequence's blocks, including an empty sequence and a partial last block."""
+    rng = np.random.default_rng(BS + Hkv + D + v_elem)
+    lens = np.array([0, 1, 17, 100, 3 * BS], np.int32)
+    NB = 40
+    max_blocks = 8
+    tables = rng.permutation(NB)[:lens.size * max_blocks].reshape(lens.size, max_blocks).astype(np.int32)
+    veb = 2 if v_elem == kv.ELEM_BF16 else 1
+    tile_k, tile_v = BS * D, BS * D * veb
+    kp = rng.integers(0, 1 << 32, size=NB * Hkv * tile_k // 4, dtype=np.uint32)
+    vp = rng.integers(0, 1 << 32, size=NB * Hkv * tile_v // 4, dtype=np.uint32)
+    k_dev = torch.from_numpy(kp.view(np.int32)).to(DEV)
+    v_dev = torch.from_numpy(vp.view(np.int32)).to(DEV)
+    h = kv.kv_cache_alloc_typed(1, NB, BS, Hkv, D, kv.ELEM_E4M3, v_elem, [1.0], [1.0], kv.DTYPE_F32, k_dev, v_dev)
+    try:
+        out = torch.full((lens.size * Hkv,), -1, dtype=torch.int32, device=DEV)
+        kv.kvf8_gather_probe(h, 0, torch.from_numpy(tables).to(DEV), max_blocks, torch.from_numpy(lens).to(DEV),
+                             lens.size, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint32)
+    finally:
+        kv.kv_cache_free(h)
+    kt = kp.reshape(NB, Hkv, tile_k // 4)
+    vt = vp.reshape(NB, Hkv, tile_v // 4)
+    for b, L in enumerate(lens):
+        blocks = tables[b, :-(-int(L) // BS)] if L > 0 else tables[b, :0]
+        for hh in range(Hkv):
+            want = np.uint32(0)
+            if blocks.size:
+                want = np.bitwise_xor.reduce(np.concatenate([kt[blocks, hh].ravel(), vt[blocks, hh].ravel()]))
+            assert int(got[b * Hkv + hh]) == int(want), (b, hh)
