@@ -180,7 +180,7 @@ def run_llama8b(args):
     decode_gbps = decode_bytes / (de_mean * 1e-3) / 1e9
     store_gbps = store_bytes / (st_mean * 1e-3) / 1e9
 
-    kernel_sha = _source_sha("decode.hip", "fp8_device.hpp", "internal.hpp")
+    kernel_sha = _source_sha("decode.hip", "fp8_device.hpp", "decode_args.hpp")
     traffic = _traffic_from_profile("decode_llama8b_pmc.txt", kernel_sha)
 
     result = {

@@ -28,7 +28,7 @@
 // that decode_reduce combines.
 
 #include "fp8_device.hpp"
-#include "internal.hpp"
+#include "decode_args.hpp"
 
 #include <cstdlib>
 

@@ -665,6 +665,7 @@ kvf8_status kvf8_gather_probe(const kvf8_cache *c, int32_t layer, const int32_t 
     a.block_tables = block_tables;
     a.seq_lens = seq_lens;
     a.out = out_words;
+    a.num_blocks = c->num_blocks;
     a.max_blocks = max_blocks;
     a.num_seqs = num_seqs;
     a.kv_heads = c->kv_heads;

@@ -7,6 +7,8 @@
 #include <cstdint>
 #include <vector>
 
+#include "decode_args.hpp"
+
 struct kvf8_cache {
     int32_t layers = 0;
     int64_t num_blocks = 0;
@@ -49,37 +51,10 @@ struct StoreArgs {
 };
 hipError_t launch_store(const StoreArgs &a, hipStream_t stream);
 
-// ---------------------------------------------------------------- decode
-struct DecodeArgs {
-    const uint16_t *q;
-    const uint8_t *k_pool;
-    const uint8_t *v_pool;
-    const int32_t *block_tables;
-    const int32_t *seq_lens;
-    void *out;
-    float *partials;         // [num_seqs][q_heads][splits][head_dim + 2] or null
-    int64_t num_blocks;      // pool blocks; table entries are clamped below it
-    int32_t max_blocks;
-    int32_t num_seqs;
-    int32_t q_heads;
-    int32_t kv_heads;
-    int32_t head_dim;
-    int32_t block_size;
-    int32_t splits;          // chunks per (seq, kv-head)
-    int32_t chunk_tokens;    // tokens per chunk (multiple of the block size)
-    float qk_scale;          // k_scale * sm_scale * log2(e)
-    float v_scale;
-    int32_t out_bf16;
-    int32_t k_eb;            // element bytes of the K / V pools: 1 (E4M3) or 2 (bf16)
-    int32_t v_eb;
-};
-// Number of splits and chunk length the decode uses for this shape.
-constexpr int kDecodeThreads = 256;   // threads per decode workgroup (4 waves)
+// ---------------------------------------------------------------- prefill constants
 constexpr int kPrefillThreads = 256;  // threads per prefill workgroup (4 waves)
 constexpr int kPrefillRows = 128;     // (query token, head) rows per prefill workgroup
-void decode_plan(int32_t num_seqs, int32_t kv_heads, int32_t head_dim, int32_t block_size,
-                 int32_t max_seq_len, int32_t *splits, int32_t *chunk_tokens);
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
 
 // ---------------------------------------------------------------- K-shift
 struct KShiftArgs {
@@ -148,6 +123,7 @@ struct GatherProbeArgs {
     const int32_t *block_tables;
     const int32_t *seq_lens;
     uint32_t *out;           // [num_seqs * kv_heads]
+    int64_t num_blocks;      // pool blocks: table entries are clamped below it
     int32_t max_blocks;
     int32_t num_seqs;
     int32_t kv_heads;

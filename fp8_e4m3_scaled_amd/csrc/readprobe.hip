@@ -69,13 +69,17 @@ __global__ __launch_bounds__(kThreads) void gather_probe(GatherProbeArgs a) {
     const int unit = blockIdx.x;
     const int seq = unit / a.kv_heads, head = unit - seq * a.kv_heads;
     const int len = a.seq_lens[seq];
-    const int64_t nblk = len > 0 ? (len + a.block_size - 1) / a.block_size : 0;
+    int64_t nblk = len > 0 ? (len + a.block_size - 1) / a.block_size : 0;
+    if (nblk > a.max_blocks) nblk = a.max_blocks;            // as the decode: never past the table row
     const int32_t *table = a.block_tables + (int64_t)seq * a.max_blocks;
     u32x4 acc = {0u, 0u, 0u, 0u};
     for (int64_t b0 = 0; b0 < nblk; b0 += kGatherIds) {
         const int nb = (int)(nblk - b0 < kGatherIds ? nblk - b0 : kGatherIds);
         __syncthreads();
-        for (int i = threadIdx.x; i < nb; i += kThreads) ids[i] = table[b0 + i];
+        for (int i = threadIdx.x; i < nb; i += kThreads) {
+            const uint32_t id = (uint32_t)table[b0 + i];          // out-of-pool ids read the last block
+            ids[i] = (int32_t)(id < a.num_blocks ? id : (uint32_t)(a.num_blocks - 1));
+        }
         __syncthreads();
         acc ^= gather_words(reinterpret_cast<const u32x4 *>(a.k_pool), ids, nb, a.k_words_log2, head, a.kv_heads);
         acc ^= gather_words(reinterpret_cast<const u32x4 *>(a.v_pool), ids, nb, a.v_words_log2, head, a.kv_heads);

@@ -378,9 +378,9 @@ kvf8_status kvf8_read_probe(const void *buf, size_t bytes, uint32_t *out_words, 
  * kv-head), the ceiling of the decode's scattered-tile access pattern.
  * Workgroup (b, kv-head h) writes the XOR of every 32-bit word of its K and V
  * tiles to out_words[b * num_kv_heads + h] (device, caller-owned).
- * block_tables, seq_lens (device) as in paged_attn_decode, with every entry
- * a valid block id (the caller's responsibility: entries are not clamped).
- * Asynchronous on `stream`.
+ * block_tables, seq_lens (device) as in paged_attn_decode; as there, block
+ * ids at or past num_blocks read the last block and a sequence never reads
+ * past its max_blocks table entries.  Asynchronous on `stream`.
  */
 kvf8_status kvf8_gather_probe(const kvf8_cache *cache, int32_t layer, const int32_t *block_tables,
                               int32_t max_blocks, const int32_t *seq_lens, int32_t num_seqs,
