@@ -6,26 +6,32 @@
 // i.e. attention over the dequantized cache with both scales moved out of
 // the inner products.  Query head h reads kv-head h / G (G = Hq / Hkv).
 //
-// Work decomposition.  Grid (split, kv-head, sequence); a workgroup of four
+// Work decomposition.  A 1-D grid of units (pair = sequence * Hkv + kv-head,
+// split), spread evenly over the 8 XCDs (decode_unit); a workgroup of four
 // waves owns one chunk of one sequence's tokens for one kv-head and all G
 // query heads of that group.  Each wave walks 32-token steps (two 16-token
 // tiles) of the chunk, interleaved with the other waves:
-//   * lane (m = lane%16, g = lane/16) loads, per tile, D/4 bytes of K (token
-//     m, column quarter g) and D/4 bytes of V (four tokens 4g..4g+3 for dims
-//     (D/16)m .. (D/16)m + D/16 - 1); in the tile layout both are contiguous,
-//     so a wave reads each tile with 16-byte loads covering it exactly;
-//   * S^T[token][head] = K Q^T on v_mfma_f32_16x16x32_bf16 (codes -> bf16 is
-//     exact); its output layout (lane (n, g) holds tokens 4g..4g+3 of head n)
-//     is exactly the B operand of the next product;
-//   * O^T[d][head] += V^T P^T on v_mfma_f32_16x16x32_f16 (codes -> f16 exact,
-//     P in f16), over 32 tokens per instruction;
+//   * lane (m = lane%16, g = lane/16) loads, per tile, D/4 elements of K
+//     (token m, column quarter g) and D/4 elements of V (four tokens
+//     4g..4g+3 for dims (D/16)m .. (D/16)m + D/16 - 1); in the tile layout
+//     both are contiguous, so a wave reads each tile with 16-byte loads
+//     covering it exactly;
+//   * S^T[token][head] = K Q^T on v_mfma_f32_16x16x32_bf16 (E4M3 codes ->
+//     bf16 is exact; a bf16 pool is the operand as stored); its output
+//     layout (lane (n, g) holds tokens 4g..4g+3 of head n) is exactly the B
+//     operand of the next product;
+//   * O^T[d][head] += V^T P^T on v_mfma_f32_16x16x32_f16 for E4M3 V (codes ->
+//     f16 exact, P in f16), or on the bf16 MFMA for a bf16 V pool with P
+//     split into two bf16 terms, over 32 tokens per instruction;
 //   * the online softmax runs in the log2 domain against a per-head reference
 //     max that only moves when a score exceeds it by more than 2^8 (lazy
 //     rescale), with per-lane partial sums.
-// The next step's K/V bytes and block ids are loaded before the current step
-// is computed.  The four waves then combine through LDS; with one split the
-// workgroup writes the output, otherwise it writes (max, sum, acc) partials
-// that decode_reduce combines.
+// The loads of the next NBUF - 1 steps are in flight in a per-lane register
+// ring (inline loads with explicit vmcnt waits for E4M3 pools); a wave's
+// block ids are preloaded.
+// The four waves then combine through LDS; with one split the workgroup
+// writes the output, otherwise it writes (max, sum, acc) partials that
+// decode_reduce combines.
 
 #include "fp8_device.hpp"
 #include "decode_args.hpp"

@@ -7,21 +7,22 @@
 // the products.]  As in the decode, s = (q . K_codes) * k_scale * sm_scale,
 // o = v_scale * softmax(s) V_codes.
 //
-// Work decomposition.  Grid (query tile, kv-head, sequence).  A "row" is one
-// (query token, head of the kv-head's group) pair; row r of a tile is token
-// r / G, head r % G, so the G heads that share a kv-head share every K/V
-// tile.  A workgroup of four waves owns 128 rows (two 16-row MFMA tiles per
-// wave) and walks the keys 0 .. last row's position in 32-token steps:
-//   * the step's K and V tiles (already in MFMA operand order in the cache)
-//     are copied once into LDS and read by all four waves;
-//   * S^T[key][row] = K Q^T on v_mfma_f32_16x16x32_bf16; its output is the
-//     B operand of O^T[d][row] += V^T P^T on v_mfma_f32_16x16x32_f16;
+// Work decomposition.  A 1-D grid of (query tile, kv-head, sequence) units,
+// a pair's tiles placed on one XCD.  A "row" is one (query token, head of the
+// kv-head's group) pair; row r of a tile is token r / G, head r % G, so the G
+// heads that share a kv-head share every K/V tile.  A workgroup of four waves
+// owns 128 rows (two 16-row MFMA tiles per wave) and walks the keys 0 .. last
+// row's position in 32-token steps:
+//   * each step's K and V tiles (already in MFMA operand order in the cache)
+//     go from HBM straight into one of four LDS stages, three steps ahead,
+//     and are read from LDS by all four waves;
+//   * S^T[key][row] = K Q^T on the fp8 MFMA with the K codes as stored and Q
+//     split exactly into two E4M3 terms (below); its output is the B operand
+//     of O^T[d][row] += V^T P^T on v_mfma_f32_16x16x32_f16;
 //   * online softmax per row in the log2 domain with the same lazy reference
 //     as the decode, P = exp2(fma(s, |qk|, -max)) from the raw MFMA scores;
 //     causal masking only on steps that reach the tile's first query
 //     position.
-// The next step's tiles are loaded into registers while the current one is
-// computed, then written to the other LDS buffer.
 
 #include "fp8_device.hpp"
 #include "internal.hpp"
@@ -285,6 +286,18 @@ void prefill_kernel(PrefillArgs a) {
     // 16i.. of the wave's 1 KiB).  Steps past the last one re-read the
     // sequence's last block (blocks_of clamps), so every step issues the same
     // CH loads and the vmcnt arithmetic below holds.
+    // A lane's CH chunks sit at fixed offsets inside their block's tile:
+    // steps start on 32-key boundaries and BS divides 32, so a tile's first
+    // in-block key is 16t mod BS at every step and only the block ids change.
+    const uint8_t *csrc[CH];
+    bool cone[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = threadIdx.x + i * kThreads;
+        csrc[i] = chunk_src<D, BS>(c, a.k_pool, a.v_pool, 0u, 0u, a.kv_heads, kvh, 0);
+        cone[i] = ((c / (StepLds<D>::TILE / 16)) & 1) != 0;
+    }
+    const int64_t blk_bytes = (int64_t)a.kv_heads * BS * D;
     auto issue = [&](int st) {
         const int p = st * kStep;
         uint32_t b0, b1;
@@ -293,8 +306,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const int c = threadIdx.x + i * kThreads;
-            load_to_lds16(chunk_src<D, BS>(c, a.k_pool, a.v_pool, b0, b1, a.kv_heads, kvh, p),
-                          stage + (c - lane) * 16);
+            load_to_lds16(csrc[i] + (int64_t)(cone[i] ? b1 : b0) * blk_bytes, stage + (c - lane) * 16);
         }
     };
 
