@@ -95,6 +95,10 @@ def _load():
         "orc_kshift": (ctypes.c_int, [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, P, i64,
                                       ctypes.c_int, f32, ctypes.c_int, ctypes.c_int]),
         "orc_kv_bytes_per_block": (i64, [ctypes.c_int] * 4),
+        "orc_kshift_typed": (ctypes.c_int, [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, P,
+                                            i64, ctypes.c_int, f32, ctypes.c_int, ctypes.c_int]),
+        "orc_kshift_per_slot_typed": (ctypes.c_int, [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                     i64, P, P, i64, f32, ctypes.c_int, ctypes.c_int]),
         "orc_kshift_per_slot": (ctypes.c_int, [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, P, P, i64,
                                                f32, ctypes.c_int, ctypes.c_int]),
         "orc_amax_bf16": (f32, [P, i64, i64, i64, f32]),
@@ -305,13 +309,14 @@ def rope_table(rot_dim: int, delta: int, theta: float):
 def kshift(k_pool, slots, *, Hkv: int, D: int, BS: int, delta: int, theta: float, rot_dim: int,
            neox: bool) -> None:
     """Re-rotate cached K by a RoPE position delta, in place (scale-free).  Slots
-    that are negative or at or past the pool's NB*BS slots are skipped."""
+    that are negative or at or past the pool's NB*BS slots are skipped.  A
+    uint8 pool holds E4M3 codes, a uint16 pool bf16 values."""
     s = _c(slots, np.int64)
-    assert k_pool.dtype == np.uint8 and k_pool.flags.c_contiguous
+    eb = _elem_bytes(k_pool)
     assert k_pool.size % (Hkv * BS * D) == 0
     NB = k_pool.size // (Hkv * BS * D)
-    rc = _load().orc_kshift(_ptr(k_pool), Hkv, D, BS, NB, _ptr(s), s.size, int(delta),
-                            float(np.float32(theta)), rot_dim, 1 if neox else 0)
+    rc = _load().orc_kshift_typed(_ptr(k_pool), eb, Hkv, D, BS, NB, _ptr(s), s.size, int(delta),
+                                  float(np.float32(theta)), rot_dim, 1 if neox else 0)
     if rc != 0:
         raise MemoryError("oracle scratch allocation failed")
 
@@ -322,10 +327,10 @@ def kshift_per_slot(k_pool, slots, deltas, *, Hkv: int, D: int, BS: int, theta: 
     s = _c(slots, np.int64)
     dl = _c(deltas, np.int32)
     assert s.shape == dl.shape
-    assert k_pool.dtype == np.uint8 and k_pool.flags.c_contiguous
+    eb = _elem_bytes(k_pool)
     assert k_pool.size % (Hkv * BS * D) == 0
     NB = k_pool.size // (Hkv * BS * D)
-    rc = _load().orc_kshift_per_slot(_ptr(k_pool), Hkv, D, BS, NB, _ptr(s), _ptr(dl), s.size,
-                                     float(np.float32(theta)), rot_dim, 1 if neox else 0)
+    rc = _load().orc_kshift_per_slot_typed(_ptr(k_pool), eb, Hkv, D, BS, NB, _ptr(s), _ptr(dl), s.size,
+                                           float(np.float32(theta)), rot_dim, 1 if neox else 0)
     if rc != 0:
         raise MemoryError("oracle scratch allocation failed")

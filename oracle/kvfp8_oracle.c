@@ -435,9 +435,15 @@ void orc_rope_table(int rot_dim, int delta, float theta, float *cos_out, float *
     }
 }
 
+uint16_t orc_f32_to_bf16_rne(float x);
+
 /* Rotate every rotary pair of one slot's K rows (all kv-heads) by the
- * angles whose fp32 cos/sin are cs[p], sn[p]. */
-static void orc_kshift_slot(uint8_t *k_pool, int Hkv, int D, int BS, int64_t slot,
+ * angles whose fp32 cos/sin are cs[p], sn[p].  eb = 1: E4M3 codes (a pair
+ * holding a NaN code becomes the NaN code in both places); eb = 2: bf16
+ * values [P3, "What turning it on costs": the bf16 twin of the cache],
+ * rotated the same way and rounded to fp32 then to the nearest bf16 (a pair
+ * holding a NaN becomes the quiet NaN 0x7FC0 in both places). */
+static void orc_kshift_slot(void *pool, int eb, int Hkv, int D, int BS, int64_t slot,
                             const float *cs, const float *sn, int rot_dim, int style)
 {
     const int64_t block = slot / BS;
@@ -447,27 +453,43 @@ static void orc_kshift_slot(uint8_t *k_pool, int Hkv, int D, int BS, int64_t slo
         for (int p = 0; p < rot_dim / 2; ++p) {
             const int d0 = style == 1 ? p : 2 * p;
             const int d1 = style == 1 ? p + rot_dim / 2 : 2 * p + 1;
-            uint8_t *c0 = &k_pool[base + orc_k_tile_offset(t, d0, BS, D)];
-            uint8_t *c1 = &k_pool[base + orc_k_tile_offset(t, d1, BS, D)];
-            const float x0 = orc_e4m3_decode(*c0);
-            const float x1 = orc_e4m3_decode(*c1);
+            const int64_t e0 = base + orc_k_tile_offset(t, d0, BS, D);
+            const int64_t e1 = base + orc_k_tile_offset(t, d1, BS, D);
+            float x0, x1;
+            if (eb == 1) {
+                x0 = orc_e4m3_decode(((uint8_t *)pool)[e0]);
+                x1 = orc_e4m3_decode(((uint8_t *)pool)[e1]);
+            } else {
+                x0 = orc_bf16_to_f32(((uint16_t *)pool)[e0]);
+                x1 = orc_bf16_to_f32(((uint16_t *)pool)[e1]);
+            }
             if (isnan(x0) || isnan(x1)) {
-                *c0 = 0x7F;
-                *c1 = 0x7F;
+                if (eb == 1) {
+                    ((uint8_t *)pool)[e0] = 0x7F;
+                    ((uint8_t *)pool)[e1] = 0x7F;
+                } else {
+                    ((uint16_t *)pool)[e0] = 0x7FC0;
+                    ((uint16_t *)pool)[e1] = 0x7FC0;
+                }
                 continue;
             }
             const double c = cs[p], s = sn[p];
             const double r0 = (double)x0 * c - (double)x1 * s;
             const double r1 = (double)x0 * s + (double)x1 * c;
-            *c0 = orc_e4m3_encode((float)r0);
-            *c1 = orc_e4m3_encode((float)r1);
+            if (eb == 1) {
+                ((uint8_t *)pool)[e0] = orc_e4m3_encode((float)r0);
+                ((uint8_t *)pool)[e1] = orc_e4m3_encode((float)r1);
+            } else {
+                ((uint16_t *)pool)[e0] = orc_f32_to_bf16_rne((float)r0);
+                ((uint16_t *)pool)[e1] = orc_f32_to_bf16_rne((float)r1);
+            }
         }
     }
 }
 
-int orc_kshift(uint8_t *k_pool, int Hkv, int D, int BS, int64_t NB,
-               const int64_t *slots, int64_t n_slots,
-               int delta, float theta, int rot_dim, int style)
+int orc_kshift_typed(void *k_pool, int eb, int Hkv, int D, int BS, int64_t NB,
+                     const int64_t *slots, int64_t n_slots,
+                     int delta, float theta, int rot_dim, int style)
 {
     float *cs = (float *)malloc(sizeof(float) * (size_t)(rot_dim / 2 + 1));
     float *sn = (float *)malloc(sizeof(float) * (size_t)(rot_dim / 2 + 1));
@@ -480,10 +502,17 @@ int orc_kshift(uint8_t *k_pool, int Hkv, int D, int BS, int64_t NB,
         const int64_t slot = slots[i];
         if (slot < 0 || slot >= NB * BS)
             continue;
-        orc_kshift_slot(k_pool, Hkv, D, BS, slot, cs, sn, rot_dim, style);
+        orc_kshift_slot(k_pool, eb, Hkv, D, BS, slot, cs, sn, rot_dim, style);
     }
     free(cs); free(sn);
     return 0;
+}
+
+int orc_kshift(uint8_t *k_pool, int Hkv, int D, int BS, int64_t NB,
+               const int64_t *slots, int64_t n_slots,
+               int delta, float theta, int rot_dim, int style)
+{
+    return orc_kshift_typed(k_pool, 1, Hkv, D, BS, NB, slots, n_slots, delta, theta, rot_dim, style);
 }
 
 /* Per-slot deltas [P1, tests/test-fp8.cpp check_fp8_context_shift: the
@@ -491,9 +520,9 @@ int orc_kshift(uint8_t *k_pool, int Hkv, int D, int BS, int64_t NB,
  * different amounts in one pass]: slot slots[i] turns by deltas[i], each
  * exactly as orc_kshift would turn it alone.  The angle table is rebuilt
  * whenever the delta changes from the previous slot's. */
-int orc_kshift_per_slot(uint8_t *k_pool, int Hkv, int D, int BS, int64_t NB,
-                        const int64_t *slots, const int32_t *deltas, int64_t n_slots,
-                        float theta, int rot_dim, int style)
+int orc_kshift_per_slot_typed(void *k_pool, int eb, int Hkv, int D, int BS, int64_t NB,
+                              const int64_t *slots, const int32_t *deltas, int64_t n_slots,
+                              float theta, int rot_dim, int style)
 {
     float *cs = (float *)malloc(sizeof(float) * (size_t)(rot_dim / 2 + 1));
     float *sn = (float *)malloc(sizeof(float) * (size_t)(rot_dim / 2 + 1));
@@ -512,10 +541,18 @@ int orc_kshift_per_slot(uint8_t *k_pool, int Hkv, int D, int BS, int64_t NB,
             orc_rope_table(rot_dim, current, theta, cs, sn);
             have = 1;
         }
-        orc_kshift_slot(k_pool, Hkv, D, BS, slot, cs, sn, rot_dim, style);
+        orc_kshift_slot(k_pool, eb, Hkv, D, BS, slot, cs, sn, rot_dim, style);
     }
     free(cs); free(sn);
     return 0;
+}
+
+int orc_kshift_per_slot(uint8_t *k_pool, int Hkv, int D, int BS, int64_t NB,
+                        const int64_t *slots, const int32_t *deltas, int64_t n_slots,
+                        float theta, int rot_dim, int style)
+{
+    return orc_kshift_per_slot_typed(k_pool, 1, Hkv, D, BS, NB, slots, deltas, n_slots, theta, rot_dim,
+                                     style);
 }
 
 /* ------------------------------------------------------------------ */

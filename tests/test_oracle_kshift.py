@@ -166,3 +166,65 @@ def test_per_slot_deltas(orc, neox):
     assert np.array_equal(got, want)
     assert np.array_equal(got, alone)
     assert not np.array_equal(got, pool)
+
+
+def _bf16_pool(rng, NB, Hkv, BS, D):
+    import torch
+    x = (rng.standard_normal((NB, Hkv, BS * D)) * np.exp(rng.uniform(-20, 20, (NB, Hkv, BS * D)))).astype(np.float32)
+    x[rng.random(x.shape) < 0.01] = 0.0
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    bits[rng.random(bits.shape) < 0.01] = 0x0003          # subnormal bf16
+    return bits
+
+
+@pytest.mark.parametrize("neox", [True, False])
+@pytest.mark.parametrize("per_slot", [False, True])
+def test_bf16_pool_rotation(orc, neox, per_slot):
+    """K-shift of a bf16 K pool (the bf16 twin of the cache): each pair is the
+    NumPy complex128 rotation of the stored values, rounded to fp32 and then to
+    bf16 by torch (independent of the oracle); delta 0 leaves finite values as
+    they are; a NaN in a pair makes both the quiet NaN 0x7FC0."""
+    import torch
+    rng = np.random.default_rng(31 + neox + 2 * per_slot)
+    NB, Hkv, BS, D, rot, theta = 4, 2, 16, 64, 48, 10000.0
+    pool = _bf16_pool(rng, NB, Hkv, BS, D)
+    slots = rng.permutation(NB * BS)[:30].astype(np.int64)
+    deltas = rng.choice(np.array([-4096, -7, 0, 3, 100], np.int32), size=slots.shape)
+    got = pool.copy()
+    if per_slot:
+        orc.kshift_per_slot(got, slots, deltas, Hkv=Hkv, D=D, BS=BS, theta=theta, rot_dim=rot, neox=neox)
+    else:
+        deltas[:] = -7
+        orc.kshift(got, slots, Hkv=Hkv, D=D, BS=BS, delta=-7, theta=theta, rot_dim=rot, neox=neox)
+    want = pool.copy()
+    half = rot // 2
+    i0 = np.arange(half) if neox else 2 * np.arange(half)
+    i1 = i0 + half if neox else i0 + 1
+    for slot, dl in zip(slots, deltas):
+        blk, t = divmod(int(slot), BS)
+        c, s = orc.rope_table(rot, int(dl), theta)
+        for h in range(Hkv):
+            ko = np.array([orc.k_tile_offset(t, d, BS, D) for d in range(D)])
+            x = orc.bf16_to_f32(pool[blk, h, ko]).astype(np.float64)
+            a = np.empty(half, np.complex128)
+            a.real, a.imag = x[i0], x[i1]
+            r = np.empty(half, np.complex128)
+            r.real, r.imag = c, s
+            z = a * r
+            row = pool[blk, h, ko].copy()
+            for idx, val in ((i0, z.real), (i1, z.imag)):
+                row[idx] = torch.from_numpy(val.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            want[blk, h, ko] = row
+    assert np.array_equal(got, want), int((got != want).sum())
+    # delta 0 keeps finite values
+    z0 = pool.copy()
+    orc.kshift(z0, slots, Hkv=Hkv, D=D, BS=BS, delta=0, theta=theta, rot_dim=rot, neox=neox)
+    assert np.array_equal(z0, pool)
+    # NaN pairs
+    nanp = pool.copy()
+    blk, t = divmod(int(slots[0]), BS)
+    e0 = orc.k_tile_offset(t, int(i0[1]), BS, D)
+    e1 = orc.k_tile_offset(t, int(i1[1]), BS, D)
+    nanp[blk, 0, e0] = 0xFFC1
+    orc.kshift(nanp, slots[:1], Hkv=Hkv, D=D, BS=BS, delta=5, theta=theta, rot_dim=rot, neox=neox)
+    assert nanp[blk, 0, e0] == 0x7FC0 and nanp[blk, 0, e1] == 0x7FC0
