@@ -522,7 +522,6 @@ kvf8_status check_rope(const kvf8_cache *c, float theta_base, int32_t rot_dim, k
         return fail(KVF8_E_INVALID, "theta_base must be finite and > 0");
     if (style != KVF8_ROPE_NORM && style != KVF8_ROPE_NEOX)
         return fail(KVF8_E_INVALID, "style must be KVF8_ROPE_NORM or KVF8_ROPE_NEOX");
-    if (c->k_eb != 1) return fail(KVF8_E_UNSUPPORTED, "kv_shift_rope needs an E4M3 K pool");
     return KVF8_OK;
 }
 }  // namespace
@@ -549,6 +548,7 @@ kvf8_status kv_shift_rope(kvf8_cache *c, int32_t layer, const int64_t *slots, in
     a.block_size = c->block_size;
     a.rot_dim = rot_dim;
     a.neox = style == KVF8_ROPE_NEOX;
+    a.k_eb = c->k_eb;
     for (int32_t i = 0; i < rot_dim / 2; ++i) rope_angle(delta, theta_base, rot_dim, i, a.cos_t[i], a.sin_t[i]);
     hipError_t e = kvf8::launch_kshift(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "kv_shift_rope launch");
@@ -597,6 +597,7 @@ kvf8_status kv_shift_rope_per_slot(kvf8_cache *c, int32_t layer, const int64_t *
     a.rows = table_rows;
     a.table = table;
     a.n_rows = n_rows;
+    a.k_eb = c->k_eb;
     hipError_t e = kvf8::launch_kshift(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "kv_shift_rope_per_slot launch");
     return ok();

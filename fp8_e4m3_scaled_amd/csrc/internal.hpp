@@ -72,6 +72,7 @@ struct KShiftArgs {
     const int32_t *rows;     // ... or a row of `table` per slot: [n_rows][rot_dim/2][cos, sin]
     const float *table;
     int32_t n_rows;
+    int32_t k_eb;            // element bytes of the K pool: 1 (E4M3 codes) or 2 (bf16 values)
 };
 hipError_t launch_kshift(const KShiftArgs &a, hipStream_t stream);
 

@@ -281,6 +281,136 @@ __global__ __launch_bounds__(kThreads) void kshift_slot_pairs(KShiftArgs a) {
     *b1 = (uint8_t)(y >> 8);
 }
 
+// ---------------------------------------------------------------- bf16 K pools
+// The bf16 twin of the cache keeps K as bf16 values at the same element
+// positions.  A pair rotates as above (fp64, products exact: 8-bit by 24-bit
+// significands) and each result is rounded to fp32, then to the nearest bf16;
+// a pair holding a NaN becomes the quiet NaN 0x7FC0 in both places.
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Two bf16 values (x0 in bits 0-15, x1 in 16-31 of the result) from a pair.
+__device__ __forceinline__ uint32_t rotate_bf16(uint32_t b0, uint32_t b1, double c, double s) {
+#pragma clang fp contract(off)
+    const float x0 = __uint_as_float(b0 << 16), x1 = __uint_as_float(b1 << 16);
+    if (__builtin_isnan(x0) || __builtin_isnan(x1)) return 0x7FC07FC0u;
+    const double a = (double)x0, b = (double)x1;
+    const float y0 = (float)__builtin_fma(a, c, -(b * s));
+    const float y1 = (float)__builtin_fma(a, s, b * c);
+    return bf16_rne(y0) | (bf16_rne(y1) << 16);
+}
+
+// Run path for bf16: a thread rotates the pairs of one 16-byte run (eight
+// elements; NEOX: eight pairs with the partner run rot/2 further, NORM: four
+// (2i, 2i+1) pairs) in every (slot, head) item j = g / RP, g / RP + J, ...
+// With one delta its cos/sin stay in registers; with a table row per slot
+// they are loaded per item.
+template <bool NEOX, bool PER_SLOT>
+__global__ __launch_bounds__(kThreads) void kshift_bf16_runs(KShiftArgs a, int rp_log2) {
+    constexpr int NP = NEOX ? 8 : 4;
+    const int D = a.head_dim, H = a.kv_heads;
+    const int half = a.rot_dim / 2;
+    const int runs = NEOX ? a.rot_dim / 16 : a.rot_dim / 8;
+    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int r = (int)(g & ((1 << rp_log2) - 1));
+    const int64_t nj = a.n_slots * H;
+    int64_t j = g >> rp_log2;
+    if (r >= runs || j >= nj) return;
+    const int64_t jstep = ((int64_t)gridDim.x * kThreads) >> rp_log2;
+    const int p0 = NEOX ? 8 * r : 4 * r;
+    const int da = 8 * r, db = da + half;
+    double cs[NP], sn[NP];
+    if (!PER_SLOT) {
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            cs[k] = (double)a.cos_t[p0 + k];
+            sn[k] = (double)a.sin_t[p0 + k];
+        }
+    }
+    uint16_t *kp = reinterpret_cast<uint16_t *>(a.k_pool);
+    for (; j < nj; j += jstep) {
+        const int64_t si = j / H;
+        const int h = (int)(j - si * H);
+        const int64_t slot = a.slots[si];
+        if (slot < 0 || slot >= a.pool_slots) continue;
+        if (PER_SLOT) {
+            const int32_t row = a.rows[si];
+            if (row < 0 || row >= a.n_rows) continue;
+            const f32x4 *tp = reinterpret_cast<const f32x4 *>(a.table + ((int64_t)row * half + p0) * 2);
+#pragma unroll
+            for (int k = 0; k < NP / 2; ++k) {
+                const f32x4 v = tp[k];
+                cs[2 * k] = (double)v[0];
+                sn[2 * k] = (double)v[1];
+                cs[2 * k + 1] = (double)v[2];
+                sn[2 * k + 1] = (double)v[3];
+            }
+        }
+        const int64_t blk = slot / a.block_size;
+        const int t = (int)(slot - blk * a.block_size);
+        uint16_t *tile = kp + (blk * H + h) * (int64_t)a.block_size * D;
+        u32x4 *pa = reinterpret_cast<u32x4 *>(tile + k_offset(t, da, a.block_size, D));
+        const u32x4 A = *pa;
+        if (NEOX) {
+            u32x4 *pb = reinterpret_cast<u32x4 *>(tile + k_offset(t, db, a.block_size, D));
+            const u32x4 B = *pb;
+            u32x4 na, nb;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t y0 = rotate_bf16(A[w] & 0xFFFFu, B[w] & 0xFFFFu, cs[2 * w], sn[2 * w]);
+                const uint32_t y1 = rotate_bf16(A[w] >> 16, B[w] >> 16, cs[2 * w + 1], sn[2 * w + 1]);
+                na[w] = (y0 & 0xFFFFu) | (y1 << 16);
+                nb[w] = (y0 >> 16) | (y1 & 0xFFFF0000u);
+            }
+            *pa = na;
+            *pb = nb;
+        } else {
+            u32x4 na;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) na[w] = rotate_bf16(A[w] & 0xFFFFu, A[w] >> 16, cs[w], sn[w]);
+            *pa = na;
+        }
+    }
+}
+
+// One pair per thread for bf16 (rotary widths the run path does not cover).
+template <bool PER_SLOT>
+__global__ __launch_bounds__(kThreads) void kshift_bf16_pairs(KShiftArgs a) {
+    const int D = a.head_dim, BS = a.block_size, H = a.kv_heads;
+    const int half = a.rot_dim / 2;
+    const int64_t item = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t total = a.n_slots * H * half;
+    if (item >= total) return;
+    const int p = (int)(item % half);
+    const int h = (int)((item / half) % H);
+    const int64_t si = item / ((int64_t)half * H);
+    const int64_t slot = a.slots[si];
+    if (slot < 0 || slot >= a.pool_slots) return;
+    float c, s;
+    if (PER_SLOT) {
+        const int32_t row = a.rows[si];
+        if (row < 0 || row >= a.n_rows) return;
+        const f32x2 v = *reinterpret_cast<const f32x2 *>(a.table + ((int64_t)row * half + p) * 2);
+        c = v[0];
+        s = v[1];
+    } else {
+        c = a.cos_t[p];
+        s = a.sin_t[p];
+    }
+    const int64_t blk = slot / BS;
+    const int t = (int)(slot - blk * BS);
+    uint16_t *tile = reinterpret_cast<uint16_t *>(a.k_pool) + (blk * H + h) * (int64_t)BS * D;
+    uint16_t *e0 = tile + k_offset(t, a.neox ? p : 2 * p, BS, D);
+    uint16_t *e1 = tile + k_offset(t, a.neox ? p + half : 2 * p + 1, BS, D);
+    const uint32_t y = rotate_bf16(*e0, *e1, (double)c, (double)s);
+    *e0 = (uint16_t)(y & 0xFFFFu);
+    *e1 = (uint16_t)(y >> 16);
+}
+
 __global__ __launch_bounds__(kThreads) void kshift_pairs(KShiftArgs a) {
     __shared__ Table tab;
     load_table(tab, a);
@@ -309,7 +439,33 @@ __global__ __launch_bounds__(kThreads) void kshift_pairs(KShiftArgs a) {
 
 }  // namespace
 
+static hipError_t launch_kshift_bf16(const KShiftArgs &a, hipStream_t stream) {
+    const bool per_slot = a.rows != nullptr;
+    const bool runs = a.neox ? (a.rot_dim % 16 == 0) : (a.rot_dim % 8 == 0);
+    if (runs) {
+        const int per_row = a.neox ? a.rot_dim / 16 : a.rot_dim / 8;
+        int rp_log2 = 0;
+        while ((1 << rp_log2) < per_row) ++rp_log2;
+        int64_t wgs = (((a.n_slots * a.kv_heads) << rp_log2) + kThreads - 1) / kThreads;
+        if (wgs > kRunsMaxWgs) wgs = kRunsMaxWgs;
+        if (wgs < 1) wgs = 1;
+        const dim3 grid((unsigned)wgs), block(kThreads);
+        if (a.neox && per_slot) hipLaunchKernelGGL((kshift_bf16_runs<true, true>), grid, block, 0, stream, a, rp_log2);
+        else if (a.neox) hipLaunchKernelGGL((kshift_bf16_runs<true, false>), grid, block, 0, stream, a, rp_log2);
+        else if (per_slot) hipLaunchKernelGGL((kshift_bf16_runs<false, true>), grid, block, 0, stream, a, rp_log2);
+        else hipLaunchKernelGGL((kshift_bf16_runs<false, false>), grid, block, 0, stream, a, rp_log2);
+        return hipGetLastError();
+    }
+    const int64_t total = a.n_slots * a.kv_heads * (a.rot_dim / 2);
+    const int64_t wgs = (total + kThreads - 1) / kThreads;
+    if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (per_slot) hipLaunchKernelGGL(kshift_bf16_pairs<true>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL(kshift_bf16_pairs<false>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_kshift(const KShiftArgs &a, hipStream_t stream) {
+    if (a.k_eb == 2) return launch_kshift_bf16(a, stream);
     const bool runs = a.neox ? (a.rot_dim % 32 == 0) : (a.rot_dim % 16 == 0);
     if (a.rows) {
         if (runs) {

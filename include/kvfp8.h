@@ -130,8 +130,10 @@ kvf8_status kv_cache_alloc(int32_t num_layers, int64_t num_blocks, int32_t block
  * index, two bytes each) and stores the given values unchanged, so its scale
  * must be 1.0 for every layer (NULL scales give 1.0; any other value ->
  * KVF8_E_SCALE).  BF16 pools support head_dim 64 and 128 (256 ->
- * KVF8_E_UNSUPPORTED).  paged_attn_prefill_chunk needs both pools E4M3 and
- * kv_shift_rope needs an E4M3 K pool (else KVF8_E_UNSUPPORTED).
+ * KVF8_E_UNSUPPORTED).  paged_attn_prefill_chunk needs both pools E4M3
+ * (else KVF8_E_UNSUPPORTED).  kv_shift_rope on a BF16 K pool rounds each
+ * rotated value to fp32 and then to the nearest bf16 (a pair holding a NaN
+ * becomes the quiet NaN 0x7FC0 in both places).
  */
 kvf8_status kv_cache_alloc_typed(int32_t num_layers, int64_t num_blocks, int32_t block_size,
                                  int32_t num_kv_heads, int32_t head_dim, kvf8_elem k_elem,
@@ -316,8 +318,8 @@ kvf8_status kv_shift_rope(kvf8_cache *cache, int32_t layer, const int64_t *slots
  *   table_rows (device): int32 [n_slots].  table (device, 16-byte aligned,
  *   caller-owned): the kv_rope_table output for n_rows deltas, copied to the
  *   device.  rot_dim and style as in kv_shift_rope (the table must have been
- *   built for the same rot_dim).  Asynchronous on `stream`; an E4M3 K pool
- *   only (KVF8_E_UNSUPPORTED otherwise).
+ *   built for the same rot_dim).  Asynchronous on `stream`.  E4M3 and bf16
+ *   K pools, each as in kv_shift_rope.
  */
 kvf8_status kv_rope_table(const int32_t *deltas, int32_t n_deltas, float theta_base, int32_t rot_dim,
                           float *table);
