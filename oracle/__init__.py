@@ -91,6 +91,9 @@ def _load():
         "orc_prefill_attn": (ctypes.c_int, [P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int, P, P, P, ctypes.c_int, ctypes.c_int,
                                             f32, f32, f64, P, i64, P]),
+        "orc_prefill_attn_typed": (ctypes.c_int, [P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, ctypes.c_int,
+                                                  ctypes.c_int, f32, f32, f64, P, i64, P]),
         "orc_rope_table": (None, [ctypes.c_int, ctypes.c_int, f32, P, P]),
         "orc_kshift": (ctypes.c_int, [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, P, i64,
                                       ctypes.c_int, f32, ctypes.c_int, ctypes.c_int]),
@@ -277,8 +280,8 @@ def prefill_attn(q_bits, k_pool, v_pool, cu_q_lens, context_lens, block_tables, 
                  sel=None) -> np.ndarray:
     """fp64 causal chunked-prefill attention over the cache. q [total_q][Hq][D] -> fp64.
 
-    sel: optional int array [n][2] of (global query index, head) pairs."""
-    assert k_pool.dtype == np.uint8 and v_pool.dtype == np.uint8, "the prefill oracle reads E4M3 pools"
+    sel: optional int array [n][2] of (global query index, head) pairs.  Pools
+    as in decode_attn: uint8 holds E4M3 codes, uint16 bf16 values."""
     q = _c(q_bits, np.uint16)
     cu = _c(cu_q_lens, np.int32)
     cl = _c(context_lens, np.int32)
@@ -290,9 +293,10 @@ def prefill_attn(q_bits, k_pool, v_pool, cu_q_lens, context_lens, block_tables, 
         sp, n = _ptr(s), s.shape[0]
     else:
         s, sp, n = None, None, 0
-    rc = _load().orc_prefill_attn(_ptr(q), Hq, _ptr(k_pool), _ptr(v_pool), Hkv, D, BS, _ptr(cu),
-                                  _ptr(cl), _ptr(bt), bt.shape[1], B, float(np.float32(k_scale)),
-                                  float(np.float32(v_scale)), float(sm_scale), sp, n, _ptr(out))
+    rc = _load().orc_prefill_attn_typed(_ptr(q), Hq, _ptr(k_pool), _ptr(v_pool), Hkv, D, BS,
+                                        _elem_bytes(k_pool), _elem_bytes(v_pool), _ptr(cu), _ptr(cl), _ptr(bt),
+                                        bt.shape[1], B, float(np.float32(k_scale)), float(np.float32(v_scale)),
+                                        float(sm_scale), sp, n, _ptr(out))
     if rc != 0:
         raise MemoryError("oracle scratch allocation failed")
     return out

@@ -365,13 +365,13 @@ int orc_decode_attn(const uint16_t *q, int Hq,
 /* <= token].  q, out: [total_q][Hq][D].                                */
 /* sel: optional list of n_sel (global query index, head) pairs.        */
 /* ------------------------------------------------------------------ */
-int orc_prefill_attn(const uint16_t *q, int Hq,
-                     const uint8_t *k_pool, const uint8_t *v_pool,
-                     int Hkv, int D, int BS,
-                     const int32_t *cu_q_lens, const int32_t *context_lens,
-                     const int32_t *block_tables, int max_blocks, int B,
-                     float k_scale, float v_scale, double sm_scale,
-                     const int64_t *sel, int64_t n_sel, double *out)
+int orc_prefill_attn_typed(const uint16_t *q, int Hq,
+                           const void *k_pool, const void *v_pool,
+                           int Hkv, int D, int BS, int k_eb, int v_eb,
+                           const int32_t *cu_q_lens, const int32_t *context_lens,
+                           const int32_t *block_tables, int max_blocks, int B,
+                           float k_scale, float v_scale, double sm_scale,
+                           const int64_t *sel, int64_t n_sel, double *out)
 {
     const int g = Hq / Hkv;
     int maxL = 0;
@@ -400,8 +400,8 @@ int orc_prefill_attn(const uint16_t *q, int Hq,
         const int L = context_lens[b] + cu_q_lens[b + 1] - cu_q_lens[b];
         const int kvh = h / g;
         if (b != cached_b || kvh != cached_h) {
-            orc_gather_dequant(k_pool, v_pool, Hkv, D, BS, block_tables + (int64_t)b * max_blocks,
-                               L, kvh, k_scale, v_scale, kd, vd);
+            orc_gather_typed(k_pool, v_pool, Hkv, D, BS, k_eb, v_eb, block_tables + (int64_t)b * max_blocks,
+                             L, kvh, k_scale, v_scale, kd, vd);
             cached_b = b;
             cached_h = kvh;
         }
@@ -410,6 +410,18 @@ int orc_prefill_attn(const uint16_t *q, int Hq,
     }
     free(kd); free(vd); free(scores);
     return 0;
+}
+
+int orc_prefill_attn(const uint16_t *q, int Hq,
+                     const uint8_t *k_pool, const uint8_t *v_pool,
+                     int Hkv, int D, int BS,
+                     const int32_t *cu_q_lens, const int32_t *context_lens,
+                     const int32_t *block_tables, int max_blocks, int B,
+                     float k_scale, float v_scale, double sm_scale,
+                     const int64_t *sel, int64_t n_sel, double *out)
+{
+    return orc_prefill_attn_typed(q, Hq, k_pool, v_pool, Hkv, D, BS, 1, 1, cu_q_lens, context_lens,
+                                  block_tables, max_blocks, B, k_scale, v_scale, sm_scale, sel, n_sel, out);
 }
 
 /* ------------------------------------------------------------------ */

@@ -119,3 +119,36 @@ def test_typed_decode_matches_fp64_sdpa(orc, keb, veb):
         other = orc.decode_attn(qb, k8, v8, w.block_tables, lens, Hq=w.Hq, Hkv=w.Hkv, D=w.D, BS=w.BS,
                                 k_scale=0.02, v_scale=0.015, sm_scale=w.sm_scale())
         assert not np.allclose(got, other, rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("keb,veb", [(1, 1), (1, 2), (2, 1), (2, 2)])
+def test_typed_prefill_matches_masked_fp64_sdpa(orc, keb, veb):
+    """Chunked prefill over every element-type combination equals torch's fp64
+    SDPA with the causal mask (query i at position ctx + i sees keys <= it),
+    over values built without the oracle."""
+    from synth import Spec
+    ctx, chunk = 37, 19
+    w = Workload("p", spec=Spec("p", 4, 2, 64, 16, [ctx, ctx + 7, 0], 4343, 0.05, 0.04, new_tokens=chunk))
+    ks = 0.05 if keb == 1 else 1.0
+    vs = 0.04 if veb == 1 else 1.0
+    kp, vp = _pools(w, keb, veb)
+    for b in range(w.B):
+        L = int(w.total_lengths[b])
+        k, v = w.kv(b, 0, L)
+        orc.store(bf16_bits(k), bf16_bits(v), w.slots(b, 0, L), kp, vp, Hkv=w.Hkv, D=w.D, BS=w.BS,
+                  k_scale=ks, v_scale=vs)
+    qb = bf16_bits(w.q_chunk())
+    cu = np.concatenate([[0], np.cumsum([chunk] * w.B)]).astype(np.int32)
+    out = orc.prefill_attn(qb, kp, vp, cu, w.lengths.astype(np.int32), w.block_tables, Hq=w.Hq, Hkv=w.Hkv,
+                           D=w.D, BS=w.BS, k_scale=ks, v_scale=vs, sm_scale=w.sm_scale())
+    g = w.Hq // w.Hkv
+    for b in range(w.B):
+        c = int(w.lengths[b])
+        L = c + chunk
+        k, v = w.kv(b, 0, L)
+        K = torch.from_numpy(_values(bf16_bits(k), keb, ks)).double().permute(1, 0, 2).repeat_interleave(g, 0)
+        V = torch.from_numpy(_values(bf16_bits(v), veb, vs)).double().permute(1, 0, 2).repeat_interleave(g, 0)
+        Q = torch.from_numpy(orc.bf16_to_f32(qb[cu[b]:cu[b + 1]])).double().permute(1, 0, 2)
+        mask = torch.arange(L)[None, :] <= (c + torch.arange(chunk)[:, None])
+        ref = F.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=w.sm_scale()).permute(1, 0, 2).numpy()
+        np.testing.assert_allclose(out[cu[b]:cu[b + 1]], ref, rtol=1e-12, atol=1e-14)
