@@ -441,19 +441,23 @@ def _cpu_baseline(w, K, V, slots, q, out, ks, vs, budget_s):
     return cpu, parity
 
 
-def _fill(w, kv, dev, stream, copies=1, upto=None, empty=False):
+def _fill(w, kv, dev, stream, copies=1, upto=None, empty=False, elems=None):
     """Store tokens 0..upto[b]-1 of every sequence into `copies` caches (untimed setup).
+    elems: (K, V) element types (default E4M3 both; a bf16 pool takes scale 1).
     Returns (pools, handles)."""
     import torch
     ks, vs, _ = w.scales()
+    ke, ve = elems if elems is not None else (kv.ELEM_E4M3, kv.ELEM_E4M3)
+    keb, veb = (1 if ke == kv.ELEM_E4M3 else 2), (1 if ve == kv.ELEM_E4M3 else 2)
     row = w.Hkv * w.D
     pools, handles = [], []
     for _ in range(copies):
         alloc = torch.empty if empty else torch.zeros
-        kp = alloc((w.NB, w.Hkv, w.BS * w.D), dtype=torch.uint8, device=dev)
-        vp = alloc((w.NB, w.Hkv, w.BS * w.D), dtype=torch.uint8, device=dev)
-        handles.append(kv.kv_cache_alloc(1, w.NB, w.BS, w.Hkv, w.D, [float(ks)], [float(vs)],
-                                         kv.DTYPE_F32, kp, vp))
+        kp = alloc((w.NB, w.Hkv, w.BS * w.D * keb), dtype=torch.uint8, device=dev)
+        vp = alloc((w.NB, w.Hkv, w.BS * w.D * veb), dtype=torch.uint8, device=dev)
+        handles.append(kv.kv_cache_alloc_typed(1, w.NB, w.BS, w.Hkv, w.D, ke, ve,
+                                               [float(ks) if keb == 1 else 1.0], [float(vs) if veb == 1 else 1.0],
+                                               kv.DTYPE_F32, kp, vp))
         pools.append((kp, vp))
     upto = w.lengths if upto is None else upto
     step = 65536
@@ -550,6 +554,28 @@ def run_prefill(args):
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = _cpu_prefill(w, q, out, ctx, n, args.cpu_seconds)
     kv.kv_cache_free(h)
+    del pools
+    # The same prefill over the bf16 twin and the mixed caches (context and
+    # chunk stored untimed): time per call and the E4M3 cache's speedup.
+    out2 = torch.empty_like(out)
+    pf_ms = float(pf.mean())
+    types = {}
+    for name, ke, ve in (("bf16_twin", kv.ELEM_BF16, kv.ELEM_BF16), ("k_e4m3_v_bf16", kv.ELEM_E4M3, kv.ELEM_BF16),
+                         ("k_bf16_v_e4m3", kv.ELEM_BF16, kv.ELEM_E4M3)):
+        tp, th = _fill(w, kv, dev, stream, elems=(ke, ve))
+        kv.kv_store_fp8(th[0], 0, K, V, row, row, sd, T, stream)
+
+        def prefill_t(i, hh=th[0]):
+            kv.paged_attn_prefill_chunk(hh, 0, q, w.Hq, cu, ctx_d, tables, w.max_blocks, w.B, T, n,
+                                        int(ctx.max()), w.sm_scale(), out2, kv.DTYPE_BF16, stream)
+
+        tt = _timed(prefill_t, args.steps, args.warmup, stream)
+        types[name] = {"ms_mean": round(float(tt.mean()), 5),
+                       "tflops": round(flops / (tt.mean() * 1e-3) / 1e12, 2),
+                       "e4m3_speedup": round(float(tt.mean()) / pf_ms, 4)}
+        kv.kv_cache_free(th[0])
+        del tp
+    res["element_types"] = types
     return res
 
 

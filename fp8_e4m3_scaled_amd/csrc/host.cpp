@@ -449,8 +449,6 @@ kvf8_status paged_attn_prefill_chunk(kvf8_cache *c, int32_t layer, const uint16_
                                      void *out, kvf8_dtype out_dtype, void *stream) {
     kvf8_status st = check_layer(c, layer);
     if (st != KVF8_OK) return st;
-    if (c->k_eb != 1 || c->v_eb != 1)
-        return fail(KVF8_E_UNSUPPORTED, "paged_attn_prefill_chunk needs E4M3 K and V pools");
     if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_ctx_len < 0 || max_blocks_per_seq < 0)
         return fail(KVF8_E_INVALID, "sizes must be >= 0");
     if (num_q_heads <= 0 || num_q_heads % c->kv_heads != 0)
@@ -498,6 +496,8 @@ kvf8_status paged_attn_prefill_chunk(kvf8_cache *c, int32_t layer, const uint16_
                     (double)a.qk_scale);
     a.v_scale = c->v_scale[layer];
     a.out_bf16 = out_dtype == KVF8_DTYPE_BF16;
+    a.k_eb = c->k_eb;
+    a.v_eb = c->v_eb;
     hipError_t e = kvf8::launch_prefill(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "paged_attn_prefill_chunk launch");
     return ok();

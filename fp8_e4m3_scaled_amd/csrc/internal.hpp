@@ -97,6 +97,8 @@ struct PrefillArgs {
     float qk_scale;          // k_scale * sm_scale * log2(e)
     float v_scale;
     int32_t out_bf16;
+    int32_t k_eb;            // element bytes of the K / V pools: 1 (E4M3) or 2 (bf16)
+    int32_t v_eb;
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 

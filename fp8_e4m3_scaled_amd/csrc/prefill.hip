@@ -50,17 +50,24 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// Bytes of one step in LDS: K tile 0, K tile 1, V tile 0, V tile 1 (16*D each).
-template <int D>
+// Bytes of one step in LDS: K tile 0, K tile 1 (16*D elements of KB bytes
+// each), V tile 0, V tile 1 (16*D elements of VB bytes).  KB, VB: 1 for E4M3
+// codes, 2 for bf16 values.
+template <int D, int KB, int VB>
 struct StepLds {
-    static constexpr int TILE = 16 * D;
-    static constexpr int BYTES = 4 * TILE;
+    static constexpr int KTILE = 16 * D * KB;
+    static constexpr int VTILE = 16 * D * VB;
+    static constexpr int BYTES = 2 * (KTILE + VTILE);
 };
 
-// Per-thread share of one step's global->LDS copy: 16-byte chunks.
-template <int D>
+// Per-thread share of one step's global->LDS copy: 16-byte chunks, rounded up
+// (a lane without a last chunk repeats its previous one, so that every lane
+// issues the same number of loads and the vmcnt arithmetic holds).
+template <int D, int KB, int VB>
 struct CopyShare {
-    static constexpr int CHUNKS = StepLds<D>::BYTES / 16 / kThreads;   // 2 (D=128), 4 (D=256), 1 (D=64)
+    static constexpr int TOTAL = StepLds<D, KB, VB>::BYTES / 16;
+    static constexpr int CHUNKS = (TOTAL + kThreads - 1) / kThreads;
+    static_assert(TOTAL % 64 == 0, "whole waves per chunk round");
 };
 
 // K/V steps in LDS: the one being computed and kStages-1 in flight.
@@ -98,44 +105,52 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Chunk c of a step (c in [0, 4*D)): tile kind (K/V), 16-key tile t, offset.
-// K tile t: 4 quarters of 16 keys x D/4 bytes; in the cache quarter q of the
-// tile's block starts at (q*BS + tb)*(D/4) with tb the tile's first in-block
-// key.  V tile t: 4 groups of 4 keys, contiguous from (tb/4)*D*4.
-template <int D, int BS>
+// Chunk c of a step (16 bytes of the step's LDS image): tile kind (K/V),
+// 16-key tile t, element offset.  K tile t: 4 quarters of 16 keys x D/4
+// elements; in the cache quarter q of the tile's block starts at element
+// (q*BS + tb)*(D/4) with tb the tile's first in-block key.  V tile t: 4 groups
+// of 4 keys, contiguous from element (tb/4)*D*4.
+template <int D, int BS, int KB, int VB>
 __device__ __forceinline__ const uint8_t *chunk_src(int c, const uint8_t *k_pool, const uint8_t *v_pool,
                                                     uint32_t blk0, uint32_t blk1, int kv_heads, int kvh,
                                                     int p) {
     constexpr int Q4 = D / 4;
-    constexpr int PER_TILE = StepLds<D>::TILE / 16;      // chunks per tile
-    const int which = c / PER_TILE;                       // 0,1: K tiles; 2,3: V tiles
-    const int off = (c % PER_TILE) * 16;                  // byte offset inside the 16*D tile image
-    const int t = which & 1;
+    constexpr int KPT = StepLds<D, KB, VB>::KTILE / 16;   // chunks per K tile
+    constexpr int VPT = StepLds<D, KB, VB>::VTILE / 16;
+    const bool is_k = c < 2 * KPT;
+    const int cc = is_k ? c : c - 2 * KPT;
+    const int t = is_k ? cc / KPT : cc / VPT;
     const uint32_t blk = t == 0 ? blk0 : blk1;
     const int tb = (p + 16 * t) % BS;
-    const int64_t base = ((int64_t)blk * kv_heads + kvh) * (BS * D);
-    if (which < 2) {
-        const int q = off / (16 * Q4);
-        const int rem = off - q * 16 * Q4;
-        return k_pool + base + (int64_t)(q * BS + tb) * Q4 + rem;
+    const int64_t base = ((int64_t)blk * kv_heads + kvh) * (BS * D);   // elements
+    if (is_k) {
+        const int e = (cc % KPT) * 16 / KB;                   // element inside the tile image
+        const int q = e / (16 * Q4);
+        const int rem = e - q * 16 * Q4;
+        return k_pool + (base + (int64_t)(q * BS + tb) * Q4 + rem) * KB;
     }
-    return v_pool + base + (int64_t)(tb / 4) * D * 4 + off;
+    const int e = (cc % VPT) * 16 / VB;
+    return v_pool + (base + (int64_t)(tb / 4) * D * 4 + e) * VB;
 }
 
-// Three waves per SIMD for head dims up to 128 (a budget of 168 VGPRs).
-template <int D>
-struct Occupancy { static constexpr int WAVES = D <= 128 ? 3 : 1; };
+// Three waves per SIMD for E4M3 pools with head dims up to 128 (a budget of
+// 168 VGPRs); two with a bf16 pool (wider operands, twice the LDS per step).
+template <int D, int KB, int VB>
+struct Occupancy { static constexpr int WAVES = D > 128 ? 1 : (KB == 1 && VB == 1 ? 3 : 2); };
 
-template <int D, int BS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<D>::WAVES)))
+template <int D, int BS, int KB, int VB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<D, KB, VB>::WAVES)))
 void prefill_kernel(PrefillArgs a) {
     constexpr int NC = D >= 128 ? D / 128 : 1;   // 128-dim K chunks per tile (D = 64: one, zero-padded)
+    constexpr int KK = D / 32;                   // bf16 K: 16x16x32 products per tile
     constexpr int MT = D / 16;
     constexpr int Q4 = D / 4;
-    constexpr int NW = D / 16;
-    constexpr int TILE = StepLds<D>::TILE;
-    constexpr int CH = CopyShare<D>::CHUNKS;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kStages][StepLds<D>::BYTES];
+    constexpr int NW = D / 16;                   // 32-bit V words per tile and lane (E4M3; twice for bf16)
+    constexpr int KTILE = StepLds<D, KB, VB>::KTILE;
+    constexpr int VTILE = StepLds<D, KB, VB>::VTILE;
+    constexpr int CH = CopyShare<D, KB, VB>::CHUNKS;
+    constexpr int TOTAL = CopyShare<D, KB, VB>::TOTAL;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kStages][StepLds<D, KB, VB>::BYTES];
 
     // Workgroups go to the 8 XCDs round-robin by linear id; every query tile
     // of pair p = seq * kv_heads + kv_head runs on XCD p % 8, the pair's tiles
@@ -179,9 +194,13 @@ void prefill_kernel(PrefillArgs a) {
     // most 2^-10, i.e. 2^-17 of the row max.  So K.(hi + lo) = 2^e (K.q) to
     // fp32 accumulation, and 2^-e goes into the row's exp2 factor.  A
     // negative qk_scale flips the sign of y (exact).
+    //
+    // With a bf16 K pool the product runs on the bf16 MFMA instead, with Q as
+    // given (sign folded in, exact) and no 2^e.
     const float qk = fabsf(a.qk_scale);
     const float qsgn = a.qk_scale < 0.0f ? -1.0f : 1.0f;
-    v8i qh[kNR][NC], ql[kNR][NC];
+    v8i qh[kNR][KB == 1 ? NC : 1], ql[kNR][KB == 1 ? NC : 1];
+    bf16x8 qb[kNR][KB == 2 ? KK : 1];
     float qk_row[kNR];
     int row_pos[kNR];          // causal limit of lane-row n in tile j (key <= row_pos)
     bool row_live[kNR];
@@ -217,44 +236,53 @@ void prefill_kernel(PrefillArgs a) {
         amax = fmaxf(amax, __shfl_xor(amax, 32));
         bad |= __shfl_xor(bad, 16);
         bad |= __shfl_xor(bad, 32);
-        int ex = 0;
-        if (!bad && amax > 0.0f) {
-            int E;
-            (void)frexpf(amax, &E);         // amax = f * 2^E, f in [0.5, 1)
-            ex = 8 - E;
-        }
-        qk_row[j] = ldexpf(qk, -ex);
-        const float mul = ldexpf(qsgn, ex);
-        uint32_t hw[D / 16], lw[D / 16];
+        if constexpr (KB == 2) {
+            qk_row[j] = qk;
 #pragma unroll
-        for (int i = 0; i < D / 16; ++i) {
-            float v[4], hv[4], rv[4];
+            for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = y[4 * i + e] * mul;     // exact: a power of two
-            int h = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-            h = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], h, true);
-            const f32x2 b01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
-            const f32x2 b23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
-            hv[0] = b01[0]; hv[1] = b01[1]; hv[2] = b23[0]; hv[3] = b23[1];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) rv[e] = v[e] - hv[e];          // exact
-            int l = __builtin_amdgcn_cvt_pk_fp8_f32(rv[0], rv[1], 0, false);
-            l = __builtin_amdgcn_cvt_pk_fp8_f32(rv[2], rv[3], l, true);
-            hw[i] = (uint32_t)h;
-            lw[i] = (uint32_t)l;
-        }
-        if (bad) {                          // a non-finite q makes the whole row NaN
-#pragma unroll
-            for (int i = 0; i < D / 16; ++i) hw[i] = 0x7F7F7F7Fu;
-        }
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int wi = 8 * c + i;
-                qh[j][c][i] = wi < D / 16 ? (int)hw[wi < D / 16 ? wi : 0] : 0;
-                ql[j][c][i] = wi < D / 16 ? (int)lw[wi < D / 16 ? wi : 0] : 0;
+                for (int e = 0; e < 8; ++e)
+                    qb[j][kk][e] = bad ? (__bf16)__builtin_nanf("") : (__bf16)(y[8 * kk + e] * qsgn);   // exact
+        } else {
+            int ex = 0;
+            if (!bad && amax > 0.0f) {
+                int E;
+                (void)frexpf(amax, &E);         // amax = f * 2^E, f in [0.5, 1)
+                ex = 8 - E;
             }
+            qk_row[j] = ldexpf(qk, -ex);
+            const float mul = ldexpf(qsgn, ex);
+            uint32_t hw[D / 16], lw[D / 16];
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i) {
+                float v[4], hv[4], rv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = y[4 * i + e] * mul;     // exact: a power of two
+                int h = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+                h = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], h, true);
+                const f32x2 b01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+                const f32x2 b23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+                hv[0] = b01[0]; hv[1] = b01[1]; hv[2] = b23[0]; hv[3] = b23[1];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rv[e] = v[e] - hv[e];          // exact
+                int l = __builtin_amdgcn_cvt_pk_fp8_f32(rv[0], rv[1], 0, false);
+                l = __builtin_amdgcn_cvt_pk_fp8_f32(rv[2], rv[3], l, true);
+                hw[i] = (uint32_t)h;
+                lw[i] = (uint32_t)l;
+            }
+            if (bad) {                          // a non-finite q makes the whole row NaN
+#pragma unroll
+                for (int i = 0; i < D / 16; ++i) hw[i] = 0x7F7F7F7Fu;
+            }
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int wi = 8 * c + i;
+                    qh[j][c][i] = wi < D / 16 ? (int)hw[wi < D / 16 ? wi : 0] : 0;
+                    ql[j][c][i] = wi < D / 16 ? (int)lw[wi < D / 16 ? wi : 0] : 0;
+                }
+        }
     }
 
     // run_max starts at a finite sentinel far below any score, so that
@@ -290,24 +318,28 @@ void prefill_kernel(PrefillArgs a) {
     // steps start on 32-key boundaries and BS divides 32, so a tile's first
     // in-block key is 16t mod BS at every step and only the block ids change.
     const uint8_t *csrc[CH];
+    int64_t cstride[CH];
+    int cdst[CH];
     bool cone[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-        const int c = threadIdx.x + i * kThreads;
-        csrc[i] = chunk_src<D, BS>(c, a.k_pool, a.v_pool, 0u, 0u, a.kv_heads, kvh, 0);
-        cone[i] = ((c / (StepLds<D>::TILE / 16)) & 1) != 0;
+        int c = threadIdx.x + i * kThreads;
+        if (c >= TOTAL) c -= kThreads;                  // whole waves: repeat the previous chunk
+        constexpr int KPT = KTILE / 16, VPT = VTILE / 16;
+        const bool is_k = c < 2 * KPT;
+        csrc[i] = chunk_src<D, BS, KB, VB>(c, a.k_pool, a.v_pool, 0u, 0u, a.kv_heads, kvh, 0);
+        cstride[i] = (int64_t)a.kv_heads * BS * D * (is_k ? KB : VB);
+        cone[i] = (is_k ? c / KPT : (c - 2 * KPT) / VPT) == 1;
+        cdst[i] = (c - lane) * 16;
     }
-    const int64_t blk_bytes = (int64_t)a.kv_heads * BS * D;
     auto issue = [&](int st) {
         const int p = st * kStep;
         uint32_t b0, b1;
         blocks_of(p, b0, b1);
         uint8_t *stage = lds[st % kStages];
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = threadIdx.x + i * kThreads;
-            load_to_lds16(csrc[i] + (int64_t)(cone[i] ? b1 : b0) * blk_bytes, stage + (c - lane) * 16);
-        }
+        for (int i = 0; i < CH; ++i)
+            load_to_lds16(csrc[i] + (int64_t)(cone[i] ? b1 : b0) * cstride[i], stage + cdst[i]);
     };
 
 #pragma unroll
@@ -334,24 +366,39 @@ void prefill_kernel(PrefillArgs a) {
         f32x4 sc[kNR][2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const u32x4 *kp = reinterpret_cast<const u32x4 *>(&lds[buf][t * TILE + (g * 16 + m) * Q4]);
-            v8i ka[NC];
+            if constexpr (KB == 2) {
+                // bf16 K: the lane's D/4 values of key m, quarter g, as KK operands
+                const bf16x8 *kp = reinterpret_cast<const bf16x8 *>(&lds[buf][t * KTILE + (g * 16 + m) * Q4 * 2]);
+                bf16x8 kb[KK];
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                u32x4 k0 = kp[2 * c], k1 = u32x4{0u, 0u, 0u, 0u};
-                if (NW > 4) k1 = kp[2 * c + 1];
-                ka[c] = v8i{(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
-                            (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
-            }
+                for (int kk = 0; kk < KK; ++kk) kb[kk] = kp[kk];
 #pragma unroll
-            for (int j = 0; j < kNR; ++j) {
-                sc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < kNR; ++j) {
+                    sc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk)
+                        sc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qb[j][kk], sc[j][t], 0, 0, 0);
+                }
+            } else {
+                const u32x4 *kp = reinterpret_cast<const u32x4 *>(&lds[buf][t * KTILE + (g * 16 + m) * Q4]);
+                v8i ka[NC];
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    sc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[c], qh[j][c], sc[j][t], 0, 0,
-                                                                                0, kUnitScale, 0, kUnitScale);
-                    sc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[c], ql[j][c], sc[j][t], 0, 0,
-                                                                                0, kUnitScale, 0, kUnitScale);
+                    u32x4 k0 = kp[2 * c], k1 = u32x4{0u, 0u, 0u, 0u};
+                    if (NW > 4) k1 = kp[2 * c + 1];
+                    ka[c] = v8i{(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
+                                (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
+                }
+#pragma unroll
+                for (int j = 0; j < kNR; ++j) {
+                    sc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) {
+                        sc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[c], qh[j][c], sc[j][t], 0,
+                                                                                    0, 0, kUnitScale, 0, kUnitScale);
+                        sc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[c], ql[j][c], sc[j][t], 0,
+                                                                                    0, 0, kUnitScale, 0, kUnitScale);
+                    }
                 }
             }
         }
@@ -391,15 +438,27 @@ void prefill_kernel(PrefillArgs a) {
                 run_max[j] = ref;
             }
         }
+        // P as the B operand of the product with V: f16 for E4M3 V; for bf16 V
+        // two bf16 terms hi + lo (16 significant bits; one bf16 alone would
+        // leave P with 8).
         f16x8 pb[kNR];
+        bf16x8 ph[kNR], pl[kNR];
 #pragma unroll
         for (int j = 0; j < kNR; ++j) {
             const float nm = -run_max[j];
             float pr[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j][i], qk_row[j], nm));
-            pb[j] = f16x8{(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3],
-                          (_Float16)pr[4], (_Float16)pr[5], (_Float16)pr[6], (_Float16)pr[7]};
+            if constexpr (VB == 2) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    ph[j][i] = (__bf16)pr[i];
+                    pl[j][i] = (__bf16)(pr[i] - (float)ph[j][i]);
+                }
+            } else {
+                pb[j] = f16x8{(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3],
+                              (_Float16)pr[4], (_Float16)pr[5], (_Float16)pr[6], (_Float16)pr[7]};
+            }
             float ps = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) ps += pr[i];
@@ -407,34 +466,71 @@ void prefill_kernel(PrefillArgs a) {
         }
         // ---- O^T += V^T P^T, V operands read now and converted once for
         // both row tiles (lane (m, g) holds keys 4g..4g+3 of dims (D/16)m..)
-        uint32_t vw[2][NW];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const u32x4 *vp = reinterpret_cast<const u32x4 *>(&lds[buf][(2 + t) * TILE + (g * D + (D / 16) * m) * 4]);
-#pragma unroll
-            for (int i = 0; i < NW / 4; ++i) {
-                const u32x4 vq = vp[i];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) vw[t][4 * i + e] = vq[e];
-            }
-        }
-        if (tail) {
+        if constexpr (VB == 2) {
+            // bf16 V: per dim the four keys are 8 bytes; a 16-byte word holds
+            // two dims, split into the operands of output tiles 2i and 2i+1
+            u32x4 vv[2][NW / 2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const int valid = total - (p + 16 * t + 4 * g);
-                const uint32_t keep = valid >= 4 ? 0xFFFFFFFFu : valid <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * valid));
+                const u32x4 *vp = reinterpret_cast<const u32x4 *>(
+                    &lds[buf][2 * KTILE + t * VTILE + (g * D + (D / 16) * m) * 4 * 2]);
 #pragma unroll
-                for (int i = 0; i < NW; ++i) vw[t][i] &= keep;
+                for (int i = 0; i < NW / 2; ++i) vv[t][i] = vp[i];
             }
-        }
+            if (tail) {
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const f16x2 e0 = codes_to_f16x2<false>(vw[0][t]), e1 = codes_to_f16x2<true>(vw[0][t]);
-            const f16x2 e2 = codes_to_f16x2<false>(vw[1][t]), e3 = codes_to_f16x2<true>(vw[1][t]);
-            const f16x8 va = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+                for (int t = 0; t < 2; ++t) {
+                    const int valid = total - (p + 16 * t + 4 * g);
+                    const uint32_t keep0 = (valid > 0 ? 0xFFFFu : 0u) | (valid > 1 ? 0xFFFF0000u : 0u);
+                    const uint32_t keep1 = (valid > 2 ? 0xFFFFu : 0u) | (valid > 3 ? 0xFFFF0000u : 0u);
+                    const u32x4 keep = {keep0, keep1, keep0, keep1};
 #pragma unroll
-            for (int j = 0; j < kNR; ++j)
-                acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[j], acc[j][t], 0, 0, 0);
+                    for (int i = 0; i < NW / 2; ++i) vv[t][i] &= keep;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NW / 2; ++i) {
+                const bf16x8 v0 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vv[0][i], vv[1][i], 0, 1, 4, 5));
+                const bf16x8 v1 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vv[0][i], vv[1][i], 2, 3, 6, 7));
+#pragma unroll
+                for (int j = 0; j < kNR; ++j) {
+                    acc[j][2 * i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, ph[j], acc[j][2 * i], 0, 0, 0);
+                    acc[j][2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, ph[j], acc[j][2 * i + 1], 0, 0, 0);
+                    acc[j][2 * i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pl[j], acc[j][2 * i], 0, 0, 0);
+                    acc[j][2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, pl[j], acc[j][2 * i + 1], 0, 0, 0);
+                }
+            }
+        } else {
+            uint32_t vw[2][NW];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const u32x4 *vp = reinterpret_cast<const u32x4 *>(
+                    &lds[buf][2 * KTILE + t * VTILE + (g * D + (D / 16) * m) * 4]);
+#pragma unroll
+                for (int i = 0; i < NW / 4; ++i) {
+                    const u32x4 vq = vp[i];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vw[t][4 * i + e] = vq[e];
+                }
+            }
+            if (tail) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int valid = total - (p + 16 * t + 4 * g);
+                    const uint32_t keep = valid >= 4 ? 0xFFFFFFFFu : valid <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * valid));
+#pragma unroll
+                    for (int i = 0; i < NW; ++i) vw[t][i] &= keep;
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const f16x2 e0 = codes_to_f16x2<false>(vw[0][t]), e1 = codes_to_f16x2<true>(vw[0][t]);
+                const f16x2 e2 = codes_to_f16x2<false>(vw[1][t]), e3 = codes_to_f16x2<true>(vw[1][t]);
+                const f16x8 va = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+#pragma unroll
+                for (int j = 0; j < kNR; ++j)
+                    acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[j], acc[j][t], 0, 0, 0);
+            }
         }
     }
     wait_vmcnt<0>();    // no LDS write may still be in flight when the workgroup ends
@@ -465,7 +561,7 @@ void prefill_kernel(PrefillArgs a) {
     }
 }
 
-template <int D, int BS>
+template <int D, int BS, int KB, int VB>
 hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
     const int G = a.q_heads / a.kv_heads;
     const int tok_per_tile = kRows / G;
@@ -474,21 +570,32 @@ hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
     PrefillArgs la = a;
     la.q_tiles = tiles;
     const uint32_t units = (uint32_t)tiles * (uint32_t)(((a.num_seqs * a.kv_heads + 7) >> 3) << 3);
-    hipLaunchKernelGGL((prefill_kernel<D, BS>), dim3(units), dim3(kThreads), 0, stream, la);
+    hipLaunchKernelGGL((prefill_kernel<D, BS, KB, VB>), dim3(units), dim3(kThreads), 0, stream, la);
     return hipGetLastError();
+}
+
+template <int D, int BS>
+hipError_t launch_types(const PrefillArgs &a, hipStream_t stream) {
+    if (a.k_eb == 1 && a.v_eb == 1) return launch_t<D, BS, 1, 1>(a, stream);
+    if constexpr (D <= 128) {       // bf16 pools hold head dims up to 128
+        if (a.k_eb == 1 && a.v_eb == 2) return launch_t<D, BS, 1, 2>(a, stream);
+        if (a.k_eb == 2 && a.v_eb == 1) return launch_t<D, BS, 2, 1>(a, stream);
+        if (a.k_eb == 2 && a.v_eb == 2) return launch_t<D, BS, 2, 2>(a, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     if (a.block_size == 16) {
-        if (a.head_dim == 64) return launch_t<64, 16>(a, stream);
-        if (a.head_dim == 128) return launch_t<128, 16>(a, stream);
-        if (a.head_dim == 256) return launch_t<256, 16>(a, stream);
+        if (a.head_dim == 64) return launch_types<64, 16>(a, stream);
+        if (a.head_dim == 128) return launch_types<128, 16>(a, stream);
+        if (a.head_dim == 256) return launch_types<256, 16>(a, stream);
     } else if (a.block_size == 32) {
-        if (a.head_dim == 64) return launch_t<64, 32>(a, stream);
-        if (a.head_dim == 128) return launch_t<128, 32>(a, stream);
-        if (a.head_dim == 256) return launch_t<256, 32>(a, stream);
+        if (a.head_dim == 64) return launch_types<64, 32>(a, stream);
+        if (a.head_dim == 128) return launch_types<128, 32>(a, stream);
+        if (a.head_dim == 256) return launch_types<256, 32>(a, stream);
     }
     return hipErrorInvalidValue;
 }

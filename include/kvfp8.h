@@ -130,8 +130,8 @@ kvf8_status kv_cache_alloc(int32_t num_layers, int64_t num_blocks, int32_t block
  * index, two bytes each) and stores the given values unchanged, so its scale
  * must be 1.0 for every layer (NULL scales give 1.0; any other value ->
  * KVF8_E_SCALE).  BF16 pools support head_dim 64 and 128 (256 ->
- * KVF8_E_UNSUPPORTED).  paged_attn_prefill_chunk needs both pools E4M3
- * (else KVF8_E_UNSUPPORTED).  kv_shift_rope on a BF16 K pool rounds each
+ * KVF8_E_UNSUPPORTED).  Store, decode and prefill read each pool with its
+ * own element type.  kv_shift_rope on a BF16 K pool rounds each
  * rotated value to fp32 and then to the nearest bf16 (a pair holding a NaN
  * becomes the quiet NaN 0x7FC0 in both places).
  */

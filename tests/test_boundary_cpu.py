@@ -263,7 +263,7 @@ def test_read_probe_host_checks():
 
 def test_typed_pools_host_rules():
     """Per-pool element types: bf16 pools keep scale 1, support head_dim <= 128, report
-    their types and byte sizes, and the prefill refuses them before any launch."""
+    their types and byte sizes."""
     E, B = kv.ELEM_E4M3, kv.ELEM_BF16
     with pytest.raises(kv.KvF8Error) as ei:
         kv.kv_cache_alloc_typed(1, 8, 16, 2, 64, B, E, [0.5], [0.5], kv.DTYPE_F32, FAKE_K, FAKE_V)
@@ -288,11 +288,6 @@ def test_typed_pools_host_rules():
                 with pytest.raises(kv.KvF8Error) as ei:
                     kv.kv_cache_set_scales(c, 0, 2.0, None)
                 assert ei.value.status == kv.E_SCALE
-            if (ke, ve) != (E, E):
-                with pytest.raises(kv.KvF8Error) as ei:
-                    kv.paged_attn_prefill_chunk(c, 0, 1 << 30, 4, 1 << 30, 1 << 30, 1 << 30, 4, 1, 8, 8,
-                                                16, 0.125, 1 << 30, kv.DTYPE_F32, 0)
-                assert ei.value.status == kv.E_UNSUPPORTED
         finally:
             kv.kv_cache_free(c)
 

@@ -139,3 +139,38 @@ def test_single_token_appends_into_bf16_pools():
         assert_close(got, c.oracle_decode(q, w.total_lengths), "bf16 append + decode")
     finally:
         c.close()
+
+
+@pytest.mark.parametrize("ke,ve", COMBOS[:3])
+@pytest.mark.parametrize("Hq,Hkv,D,BS", [(4, 2, 64, 16), (32, 8, 128, 16), (16, 2, 128, 32), (12, 4, 64, 32)])
+def test_typed_prefill(ke, ve, Hq, Hkv, D, BS):
+    """Chunked prefill over bf16 and mixed pools: contexts of 0 and ragged
+    lengths, chunks of 1, straddling and empty, a ragged last key step, fp32
+    and bf16 outputs, against the oracle's attention over the same pools."""
+    ctx = np.array([0, 37, 100, 5, 64], np.int32)
+    chunks = np.array([21, 50, 1, 0, 160], np.int32)
+    spec = Spec("typedpf", Hq, Hkv, D, BS, list(ctx + chunks), 5300 + Hq + D + BS + 10 * ke + ve, 0.04, 0.03)
+    w = Workload("typedpf", spec=spec)
+    log(f"typed prefill k={ke} v={ve} Hq={Hq} Hkv={Hkv} D={D} BS={BS}")
+    c = TypedCache(w, ke, ve, 0.04, 0.03)
+    try:
+        c.check_bytes()
+        cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+        g = torch.Generator().manual_seed(77 + D)
+        q = torch.randn((int(cu[-1]), Hq, D), generator=g).to(torch.bfloat16)
+        want = oracle.prefill_attn(bf16_bits(q), c.ok, c.ov, cu, ctx, w.block_tables, Hq=Hq, Hkv=Hkv, D=D, BS=BS,
+                                   k_scale=c.ks, v_scale=c.vs, sm_scale=w.sm_scale())
+        tables = t_dev(w.block_tables.astype(np.int32))
+        for out_dtype in (kv.DTYPE_F32, kv.DTYPE_BF16):
+            dt = torch.float32 if out_dtype == kv.DTYPE_F32 else torch.bfloat16
+            out = torch.full((int(cu[-1]), Hq, D), float("nan"), dtype=dt, device=DEV)
+            kv.paged_attn_prefill_chunk(c.handle, 0, q.to(DEV), Hq, t_dev(cu), t_dev(ctx), tables, w.max_blocks,
+                                        w.B, int(cu[-1]), int(chunks.max()), int(ctx.max()), w.sm_scale(), out,
+                                        out_dtype)
+            torch.cuda.synchronize()
+            got = out.float().cpu().numpy()
+            assert_close(got, want, f"typed prefill k={ke} v={ve} out={out_dtype}")
+            if out_dtype == kv.DTYPE_F32:
+                assert float(np.max(np.abs(got - want))) <= ATOL
+    finally:
+        c.close()
