@@ -8,7 +8,8 @@ from the seeded generators on the GPU and reach both sides as the same bf16
 bits; no expected value comes from the HIP library), and
   * the whole K and V pools must equal the oracle's bit for bit;
   * attention outputs satisfy |gpu - oracle| <= 2e-3 + 1e-2 |oracle|:
-    every (sequence, head) of the Llama-shaped and variable-length decodes and
+    every (sequence, head) of the Llama-shaped decode (E4M3 and its bf16
+    twin) and of the variable-length decode and
     of both long-context decodes, and 8,192 prefill (query, head) rows that
     include the first and last 32 query tokens of every sequence (all heads).
 Oracle calls run on a thread pool over disjoint sequences / groups (the C
@@ -49,14 +50,16 @@ def _pmap(fn, items):
 class FullCache:
     """A full-size one-layer cache over torch-owned zeroed pools."""
 
-    def __init__(self, w: Workload):
+    def __init__(self, w: Workload, elems=(kv.ELEM_E4M3, kv.ELEM_E4M3)):
         self.w = w
         ks, vs, _ = w.scales()
-        self.ks, self.vs = np.float32(ks), np.float32(vs)
-        self.k_pool = torch.zeros((w.NB, w.Hkv, w.BS * w.D), dtype=torch.uint8, device=DEV)
-        self.v_pool = torch.zeros_like(self.k_pool)
-        self.handle = kv.kv_cache_alloc(1, w.NB, w.BS, w.Hkv, w.D, [float(ks)], [float(vs)],
-                                        kv.DTYPE_F32, self.k_pool, self.v_pool)
+        self.keb, self.veb = (1 if elems[0] == kv.ELEM_E4M3 else 2), (1 if elems[1] == kv.ELEM_E4M3 else 2)
+        self.ks = np.float32(ks if self.keb == 1 else 1.0)     # a bf16 pool keeps scale 1
+        self.vs = np.float32(vs if self.veb == 1 else 1.0)
+        self.k_pool = torch.zeros((w.NB, w.Hkv, w.BS * w.D * self.keb), dtype=torch.uint8, device=DEV)
+        self.v_pool = torch.zeros((w.NB, w.Hkv, w.BS * w.D * self.veb), dtype=torch.uint8, device=DEV)
+        self.handle = kv.kv_cache_alloc_typed(1, w.NB, w.BS, w.Hkv, w.D, elems[0], elems[1], [float(self.ks)],
+                                              [float(self.vs)], kv.DTYPE_F32, self.k_pool, self.v_pool)
 
     def fill(self, upto):
         """Tokens 0..upto[b]-1 of every sequence, in the benchmark's store calls."""
@@ -72,7 +75,8 @@ class FullCache:
 
     def pools(self):
         torch.cuda.synchronize()
-        return self.k_pool.cpu().numpy(), self.v_pool.cpu().numpy()
+        views = {1: np.uint8, 2: np.uint16}
+        return (self.k_pool.cpu().numpy().view(views[self.keb]), self.v_pool.cpu().numpy().view(views[self.veb]))
 
     def close(self):
         if self.handle:
@@ -83,10 +87,11 @@ class FullCache:
 class OraclePools:
     """Full-size oracle pools: every sequence's tokens [lo, hi) stored by the oracle."""
 
-    def __init__(self, w: Workload, ks, vs):
+    def __init__(self, w: Workload, ks, vs, keb=1, veb=1):
         self.w, self.ks, self.vs = w, ks, vs
-        self.kp = np.zeros((w.NB, w.Hkv, w.BS * w.D), np.uint8)
-        self.vp = np.zeros_like(self.kp)
+        types = {1: np.uint8, 2: np.uint16}
+        self.kp = np.zeros((w.NB, w.Hkv, w.BS * w.D), types[keb])
+        self.vp = np.zeros((w.NB, w.Hkv, w.BS * w.D), types[veb])
 
     def store(self, ranges):
         """ranges: (b, lo, hi) triples; different sequences write disjoint slots."""
@@ -105,7 +110,7 @@ class OraclePools:
         gk, gv = cache.pools()
         nk = int(np.count_nonzero(gk != self.kp))
         nv = int(np.count_nonzero(gv != self.vp))
-        assert nk == 0 and nv == 0, f"{what}: {nk} K and {nv} V bytes differ from the oracle"
+        assert nk == 0 and nv == 0, f"{what}: {nk} K and {nv} V elements differ from the oracle"
 
     def decode_all(self, q_bits, lens):
         """Oracle decode of every (sequence, head): [B][Hq][D] fp64."""
@@ -134,11 +139,14 @@ def _decode_full(w, cache, q, lens):
     return out.float().cpu().numpy(), ws_bytes
 
 
-def test_llama8b_full_size():
+@pytest.mark.parametrize("elems", [(kv.ELEM_E4M3, kv.ELEM_E4M3), (kv.ELEM_BF16, kv.ELEM_BF16)],
+                         ids=["e4m3", "bf16_twin"])
+def test_llama8b_full_size(elems):
     """64 x 4096 tokens, 32 q / 8 kv heads, D 128, block 16: one store launch
-    over all 262,144 tokens, one decode launch; all bytes, all 2,048 heads."""
+    over all 262,144 tokens, one decode launch; all bytes, all 2,048 heads.
+    Also for the bf16 twin the benchmark compares the E4M3 cache against."""
     w = Workload("llama8b", device=DEV)
-    cache = FullCache(w)
+    cache = FullCache(w, elems)
     try:
         row = w.Hkv * w.D
         T = int(w.total_lengths.sum())
@@ -152,13 +160,13 @@ def test_llama8b_full_size():
             K[pos:pos + L], V[pos:pos + L] = k.reshape(L, row), v.reshape(L, row)
             slots[pos:pos + L] = w.slots(b, 0, L)
             pos += L
-        log(f"llama8b full: one store of {T} tokens, one decode of {w.B} sequences")
+        log(f"llama8b full ({elems}): one store of {T} tokens, one decode of {w.B} sequences")
         kv.kv_store_fp8(cache.handle, 0, K, V, row, row, t_dev(slots), T)
         del K, V
         q = w.q_decode(DEV)
         got, ws_bytes = _decode_full(w, cache, q, w.total_lengths)
         assert ws_bytes == 0                       # the benchmark's plan: one chunk per sequence
-        orc = OraclePools(w, cache.ks, cache.vs)
+        orc = OraclePools(w, cache.ks, cache.vs, cache.keb, cache.veb)
         orc.store([(b, 0, int(w.total_lengths[b])) for b in range(w.B)])
         orc.check_bytes(cache, "llama8b")
         want = orc.decode_all(bf16_bits(q), w.total_lengths)
