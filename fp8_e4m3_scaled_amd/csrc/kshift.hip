@@ -31,7 +31,7 @@ namespace kvf8 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRunsUnroll = 2;            // (slot, head) items in flight per lane
+constexpr int kRunsUnroll = 1;            // (slot, head) items per lane per iteration (2-4 measured slower)
 constexpr int64_t kRunsMaxWgs = 4096;     // 16 workgroups per CU
 
 struct Table {
@@ -122,7 +122,8 @@ __device__ __forceinline__ void rotate_runs(const u32x4 &wa, const u32x4 &wb, co
 // a power of two; lanes with r >= runs idle) of the (slot, head) items
 // j = g / RP, g / RP + J, ... with J = grid threads / RP, so its rotary pairs
 // never change: their cos/sin are held in registers.  U items are loaded per
-// iteration to keep several 16-byte loads in flight per lane.
+// iteration (U = 1: more loads in flight per lane measured slower, as in the
+// streaming-read probe).
 template <bool NEOX, int U>
 __global__ __launch_bounds__(kThreads) void kshift_runs(KShiftArgs a, int rp_log2) {
     constexpr int NP = NEOX ? 16 : 8;      // rotary pairs per run
@@ -196,7 +197,8 @@ __global__ __launch_bounds__(kThreads) void kshift_runs(KShiftArgs a, int rp_log
 // (a.rows[si] into a.table, [row][pair][cos, sin] fp32).  Thread g works on
 // run r = g mod RP of slots g / RP, g / RP + J, ...; for each slot it loads its
 // run's cos/sin once (16-byte loads of the interleaved row) and rotates that
-// run in every kv-head, two heads in flight.
+// run in every kv-head, one head after the other (two heads in flight, or
+// (slot, head) items with a table load each, measured slower).
 template <bool NEOX>
 __global__ __launch_bounds__(kThreads) void kshift_slot_runs(KShiftArgs a, int rp_log2) {
     constexpr int NP = NEOX ? 16 : 8;
@@ -230,26 +232,15 @@ __global__ __launch_bounds__(kThreads) void kshift_slot_runs(KShiftArgs a, int r
         const int64_t oa0 = k_offset(t, da, a.block_size, D), ob0 = k_offset(t, db, a.block_size, D);
         const int64_t head_bytes = ((int64_t)1 << bs_log2) * D;
         uint8_t *base = a.k_pool + blk * H * head_bytes;
-        for (int h = 0; h < H; h += 2) {
-            const bool two = h + 1 < H;
+        for (int h = 0; h < H; ++h) {
             uint8_t *t0 = base + h * head_bytes;
-            uint8_t *t1 = t0 + head_bytes;
-            u32x4 wa0, wb0 = {0u, 0u, 0u, 0u}, wa1 = {0u, 0u, 0u, 0u}, wb1 = {0u, 0u, 0u, 0u};
-            wa0 = *reinterpret_cast<const u32x4 *>(t0 + oa0);
-            if (NEOX) wb0 = *reinterpret_cast<const u32x4 *>(t0 + ob0);
-            if (two) {
-                wa1 = *reinterpret_cast<const u32x4 *>(t1 + oa0);
-                if (NEOX) wb1 = *reinterpret_cast<const u32x4 *>(t1 + ob0);
-            }
+            const u32x4 wa = *reinterpret_cast<const u32x4 *>(t0 + oa0);
+            u32x4 wb = {0u, 0u, 0u, 0u};
+            if (NEOX) wb = *reinterpret_cast<const u32x4 *>(t0 + ob0);
             u32x4 na, nb;
-            rotate_runs<NEOX, NP>(wa0, wb0, cs, sn, na, nb);
+            rotate_runs<NEOX, NP>(wa, wb, cs, sn, na, nb);
             *reinterpret_cast<u32x4 *>(t0 + oa0) = na;
             if (NEOX) *reinterpret_cast<u32x4 *>(t0 + ob0) = nb;
-            if (two) {
-                rotate_runs<NEOX, NP>(wa1, wb1, cs, sn, na, nb);
-                *reinterpret_cast<u32x4 *>(t1 + oa0) = na;
-                if (NEOX) *reinterpret_cast<u32x4 *>(t1 + ob0) = nb;
-            }
         }
     }
 }
