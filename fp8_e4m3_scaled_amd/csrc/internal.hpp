@@ -112,7 +112,7 @@ struct CalibArgs {
     int64_t runs_per_row;    // 16-byte runs (8 elements) per row
     uint32_t *amax;          // [2] running maxima as fp32 bit patterns
 };
-constexpr int64_t kCalibWorkgroups = 1024;   // amax workgroups per launch, over both tensors
+constexpr int64_t kCalibWorkgroups = 2048;   // amax workgroups per launch, over both tensors (512-8192 swept)
 // amax over the sides present (sides = 0, 1 or 2), then, when scales_out is
 // non-null, the two scales from the maxima (fp32 or bf16 bit patterns).
 hipError_t launch_calibrate(const CalibArgs &a, int32_t sides, void *scales_out, int32_t out_bf16,
