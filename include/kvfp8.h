@@ -219,16 +219,19 @@ size_t paged_attn_decode_workspace(const kvf8_cache *cache, int32_t num_seqs,
  * For sequence b and query head h (kv-head h / (num_q_heads/num_kv_heads)):
  *   s_t = (q . K_t) * k_scale * sm_scale      over t < seq_lens[b],
  *   o   = v_scale * sum_t softmax(s)_t V_t,
- * where K_t, V_t are the stored codes' E4M3 values; this equals attention
+ * where K_t, V_t are the stored elements' values (E4M3 codes' values, or
+ * bf16 values in a bf16 pool, whose scale is 1); this equals attention
  * over the dequantized cache [P1, build_attn_scale_kv_inputs /
  * build_attn_scale_kv_output: (Q*s)(K/s) = QK, P(V/s)s = PV].
- * seq_lens[b] == 0 gives a zero row.
+ * seq_lens[b] <= 0 gives a zero row.
  *
  * q_bf16 (device): [num_seqs][num_q_heads][head_dim] bf16.
  * block_tables (device): int32 [num_seqs][max_blocks_per_seq]; entries
  *   0 .. ceil(seq_lens[b]/block_size)-1 of row b must be valid block ids.
- * seq_lens (device): int32 [num_seqs], each 0 .. max_seq_len and at most
- *   max_blocks_per_seq * block_size.
+ * seq_lens (device): int32 [num_seqs], each at most max_seq_len and at most
+ *   max_blocks_per_seq * block_size.  A longer length is out of contract: the
+ *   call still reads only the row's table entries and the pools, but that
+ *   row's result is unspecified.
  * max_seq_len (host): upper bound of seq_lens, sizes the launch.
  * sm_scale: softmax scale, finite and > 0 (usually 1/sqrt(head_dim)); the
  *   fp32 factor k_scale * sm_scale * log2(e) must be finite and nonzero

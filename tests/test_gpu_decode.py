@@ -210,3 +210,22 @@ def test_decode_routing_mutations_are_caught():
         assert_close(f.decode(q.to(DEV), f.lens), want, "unmutated")
     finally:
         f.close()
+
+
+def test_decode_empty_and_negative_lengths_with_splits():
+    """Lengths 0 and below give zero rows, also when the launch is split and the
+    reduce combines partials (no split produced anything for those rows)."""
+    spec = Spec("emptysplit", 16, 2, 128, 16, [6000, 0, 17, 4100], 4200, 0.03, 0.03)
+    w = Workload("emptysplit", spec=spec)
+    f = Filled(w)
+    try:
+        lens = np.array([6000, 0, 17, -3], np.int32)
+        assert kv.paged_attn_decode_workspace(f.cache.handle, w.B, w.Hq, 6000) > 0
+        q = w.q_decode()
+        got = f.decode(q.to(DEV), lens)
+        assert np.all(got[1] == 0.0) and np.all(got[3] == 0.0)
+        want = f.oracle_decode(bf16_bits(q), np.maximum(lens, 0))
+        for b in (0, 2):
+            assert_close(got[b], want[b], f"split decode b={b}")
+    finally:
+        f.close()
