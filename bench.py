@@ -746,6 +746,15 @@ def run_varlen(args):
     res["roofline"] = {"bound": "hbm", "achieved": round(de_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                        "frac": round(de_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                        "kernel": "decode_kernel<128,16,1,1> + decode_reduce<128>"}
+    # Beside the linear-stream ceiling: a plain read of the same tiles with one
+    # workgroup per (sequence, kv-head) and no split, which the decode's split
+    # plan beats on this length mix (long sequences would serialize).
+    kv_bytes = int(lens.astype(np.int64).sum()) * 2 * w.Hkv * w.D
+    res["stream_read_ceiling"] = _stream_ceiling(kv, stream)
+    res["decode"]["frac_of_stream_ceiling"] = round(de_gbps / res["stream_read_ceiling"]["GBps"], 4)
+    res["paged_gather_unsplit"] = _gather_ceiling(args, kv, [h], tables, w.max_blocks, lens_d, w.B, w.Hkv,
+                                                  kv_bytes, stream)
+    res["decode"]["speedup_over_unsplit_gather"] = round(de_gbps / res["paged_gather_unsplit"]["GBps"], 4)
     kv.kv_cache_free(h)
     return res
 
