@@ -36,7 +36,6 @@
 #include "fp8_device.hpp"
 #include "decode_args.hpp"
 
-#include <cstdlib>
 
 namespace kvf8 {
 namespace {
@@ -512,13 +511,6 @@ hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-int env_int(const char *name, int dflt) {
-    const char *s = std::getenv(name);
-    if (!s || !*s) return dflt;
-    const int v = std::atoi(s);
-    return v > 0 ? v : dflt;
-}
-
 }  // namespace
 
 // Chunking: at most `max_chunk` tokens per workgroup (bounds the tail of
@@ -527,8 +519,9 @@ int env_int(const char *name, int dflt) {
 void decode_plan(int32_t num_seqs, int32_t kv_heads, int32_t head_dim, int32_t block_size,
                  int32_t max_seq_len, int32_t *splits, int32_t *chunk_tokens) {
     // a wave holds the block ids of at most 64 tiles (32 steps): chunk <= 4096 tokens
-    static const int max_chunk = min(env_int("KVF8_DECODE_MAX_CHUNK", 4096), 32 * kStep * kWaves);
-    static const int target_wgs = env_int("KVF8_DECODE_TARGET_WGS", 512);
+    // (2048-token chunks and 1024 or 2048 target workgroups measured no faster)
+    constexpr int max_chunk = 32 * kStep * kWaves;
+    constexpr int target_wgs = 512;
     const int round = kStep * kWaves;
     const int64_t pairs = (int64_t)num_seqs * kv_heads;
     int64_t s = (max_seq_len + max_chunk - 1) / max_chunk;
