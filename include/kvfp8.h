@@ -20,6 +20,9 @@
  *     ordinary host memory read before the call returns.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Kernels are enqueued on it and the call returns without waiting.
+ *     Only kv_cache_alloc (when it allocates the pools) and kv_cache_free
+ *     allocate, set or synchronize device memory; every other call only
+ *     launches kernels, so it can be recorded into a HIP graph.
  *   - bf16 tensors are passed as their raw 16-bit patterns (uint16_t).
  *   - A cache handle is not thread-safe; callers serialize calls on one
  *     handle.  Calls that overlap on a stream ordering basis follow normal
