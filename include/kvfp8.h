@@ -30,7 +30,8 @@
  *
  * Cache layout.  Per layer a K pool and a V pool, each
  *   [num_blocks][num_kv_heads][block_size * head_dim] bytes,
- * one OCP E4M3 code per element.  Slot s is token s % block_size of block
+ * one OCP E4M3 code per element (or, in a pool created as bf16 by
+ * kv_cache_alloc_typed, one bf16 value per element at the same index).  Slot s is token s % block_size of block
  * s / block_size.  Inside one (block, kv-head) tile of block_size*head_dim
  * bytes the order is chosen for the matrix cores:
  *   K byte (t, d) at ((d / (D/4)) * BS + t) * (D/4) + d % (D/4)
