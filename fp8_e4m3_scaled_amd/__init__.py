@@ -33,6 +33,7 @@ SIGNATURES = {
     "kv_cache_alloc_typed": (I32, [I32, I64, I32, I32, I32, I32, I32, P, P, I32, P, P, ctypes.POINTER(P)]),
     "kv_cache_elem_types": (I32, [P, P, P]),
     "kv_cache_free": (I32, [P]),
+    "kv_cache_set_checked": (I32, [P, I32]),
     "kv_cache_set_scales": (I32, [P, I32, P, P, I32]),
     "kv_cache_get_scales": (I32, [P, I32, P, P]),
     "kv_cache_pools": (I32, [P, I32, P, P, P]),
@@ -165,6 +166,10 @@ def kv_cache_elem_types(cache):
 
 def kv_cache_free(cache) -> None:
     _check(_lib.kv_cache_free(cache))
+
+
+def kv_cache_set_checked(cache, on: bool) -> None:
+    _check(_lib.kv_cache_set_checked(cache, 1 if on else 0))
 
 
 def kv_cache_set_scales(cache, layer: int, k_scale=None, v_scale=None,

@@ -35,6 +35,45 @@ kvf8_status hip_fail(hipError_t e, const char *what) {
     return fail(KVF8_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Checked mode: read back the flag word of a check launched on `stream` and
+// wait for it (the only synchronizing step besides allocation).
+kvf8_status check_result(const kvf8_cache *c, hipError_t launched, hipStream_t stream, uint32_t *flags) {
+    if (launched != hipSuccess) return hip_fail(launched, "checked mode: check launch");
+    uint32_t h = 0;
+    hipError_t e = hipMemcpyAsync(&h, c->check_state, sizeof h, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "checked mode: read-back");
+    *flags = h;
+    return KVF8_OK;
+}
+
+// Checked mode: a slot list must not repeat an in-pool slot.
+kvf8_status check_slot_list(const kvf8_cache *c, const int64_t *slots, int64_t n, hipStream_t stream) {
+    if (!c->checked || n == 0) return KVF8_OK;
+    uint32_t flags = 0;
+    kvf8_status st = check_result(c, kvf8::launch_check_slots(c->check_state, c->check_bitmap_words, slots, n,
+                                                              c->num_blocks * c->block_size, stream),
+                                  stream, &flags);
+    if (st != KVF8_OK) return st;
+    if (flags & kvf8::kCheckRepeatedSlot)
+        return fail(KVF8_E_INVALID, "checked mode: a slot appears more than once in this call");
+    return KVF8_OK;
+}
+
+// Checked mode: lengths within their stated bounds and the table row; every
+// table entry a sequence uses inside the pool.
+kvf8_status check_table_args(const kvf8_cache *c, const kvf8::CheckTablesArgs &a, hipStream_t stream) {
+    if (!c->checked || a.num_seqs == 0) return KVF8_OK;
+    uint32_t flags = 0;
+    kvf8_status st = check_result(c, kvf8::launch_check_tables(c->check_state, a, stream), stream, &flags);
+    if (st != KVF8_OK) return st;
+    if (flags & kvf8::kCheckLength)
+        return fail(KVF8_E_INVALID, "checked mode: a sequence length exceeds its stated bound or its table row");
+    if (flags & kvf8::kCheckBlockId)
+        return fail(KVF8_E_INVALID, "checked mode: a block table entry in use lies outside the pool");
+    return KVF8_OK;
+}
+
 // Scale intake: bf16 bit patterns widen exactly to fp32 (the top 16 bits).
 float read_scale(const void *p, int32_t i, kvf8_dtype dt) {
     if (dt == KVF8_DTYPE_F32) {
@@ -216,8 +255,39 @@ kvf8_status kv_cache_free(kvf8_cache *c) {
         hipError_t e2 = hipFree(c->v_base);
         e = e1 != hipSuccess ? e1 : e2;
     }
+    if (c->check_state) {
+        hipError_t e3 = hipFree(c->check_state);
+        if (e == hipSuccess) e = e3;
+    }
     delete c;
     if (e != hipSuccess) return hip_fail(e, "hipFree");
+    return ok();
+}
+
+kvf8_status kv_cache_set_checked(kvf8_cache *c, int32_t on) {
+    if (!c) return fail(KVF8_E_INVALID, "cache is NULL");
+    if (on) {
+        if (!c->check_state) {
+            const int64_t words = (c->num_blocks * c->block_size + 31) / 32;
+            hipError_t e = hipMalloc(reinterpret_cast<void **>(&c->check_state), (size_t)(words + 1) * sizeof(uint32_t));
+            if (e != hipSuccess) {
+                c->check_state = nullptr;
+                (void)hipGetLastError();
+                return fail(KVF8_E_NOMEM, "checked mode: %lld bytes of check state: %s",
+                            (long long)((words + 1) * 4), hipGetErrorString(e));
+            }
+            c->check_bitmap_words = words;
+        }
+        c->checked = true;
+        return ok();
+    }
+    c->checked = false;
+    if (c->check_state) {
+        hipError_t e = hipFree(c->check_state);
+        c->check_state = nullptr;
+        c->check_bitmap_words = 0;
+        if (e != hipSuccess) return hip_fail(e, "hipFree");
+    }
     return ok();
 }
 
@@ -362,6 +432,8 @@ kvf8_status kv_store_fp8(kvf8_cache *c, int32_t layer, const uint16_t *k_bf16,
     a.kv_heads = c->kv_heads;
     a.head_dim = c->head_dim;
     a.block_size = c->block_size;
+    st = check_slot_list(c, slot_mapping, num_tokens, static_cast<hipStream_t>(stream));
+    if (st != KVF8_OK) return st;
     hipError_t e = kvf8::launch_store(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "kv_store_fp8 launch");
     return ok();
@@ -436,6 +508,18 @@ kvf8_status paged_attn_decode(kvf8_cache *c, int32_t layer, const uint16_t *q_bf
     a.out_bf16 = out_dtype == KVF8_DTYPE_BF16;
     a.k_eb = c->k_eb;
     a.v_eb = c->v_eb;
+    {
+        kvf8::CheckTablesArgs ca{};
+        ca.block_tables = block_tables;
+        ca.seq_lens = seq_lens;
+        ca.num_blocks = c->num_blocks;
+        ca.max_blocks = max_blocks_per_seq;
+        ca.num_seqs = num_seqs;
+        ca.block_size = c->block_size;
+        ca.max_len = max_seq_len;
+        st = check_table_args(c, ca, static_cast<hipStream_t>(stream));
+        if (st != KVF8_OK) return st;
+    }
     hipError_t e = kvf8::launch_decode(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "paged_attn_decode launch");
     return ok();
@@ -498,6 +582,21 @@ kvf8_status paged_attn_prefill_chunk(kvf8_cache *c, int32_t layer, const uint16_
     a.out_bf16 = out_dtype == KVF8_DTYPE_BF16;
     a.k_eb = c->k_eb;
     a.v_eb = c->v_eb;
+    {
+        kvf8::CheckTablesArgs ca{};
+        ca.block_tables = block_tables;
+        ca.cu_q_lens = cu_q_lens;
+        ca.context_lens = context_lens;
+        ca.num_blocks = c->num_blocks;
+        ca.total_q = total_q;
+        ca.max_blocks = max_blocks_per_seq;
+        ca.num_seqs = num_seqs;
+        ca.block_size = c->block_size;
+        ca.max_q_len = max_q_len;
+        ca.max_ctx_len = max_ctx_len;
+        st = check_table_args(c, ca, static_cast<hipStream_t>(stream));
+        if (st != KVF8_OK) return st;
+    }
     hipError_t e = kvf8::launch_prefill(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "paged_attn_prefill_chunk launch");
     return ok();
@@ -550,6 +649,8 @@ kvf8_status kv_shift_rope(kvf8_cache *c, int32_t layer, const int64_t *slots, in
     a.neox = style == KVF8_ROPE_NEOX;
     a.k_eb = c->k_eb;
     for (int32_t i = 0; i < rot_dim / 2; ++i) rope_angle(delta, theta_base, rot_dim, i, a.cos_t[i], a.sin_t[i]);
+    st = check_slot_list(c, slots, n_slots, static_cast<hipStream_t>(stream));
+    if (st != KVF8_OK) return st;
     hipError_t e = kvf8::launch_kshift(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "kv_shift_rope launch");
     return ok();
@@ -598,6 +699,8 @@ kvf8_status kv_shift_rope_per_slot(kvf8_cache *c, int32_t layer, const int64_t *
     a.table = table;
     a.n_rows = n_rows;
     a.k_eb = c->k_eb;
+    st = check_slot_list(c, slots, n_slots, static_cast<hipStream_t>(stream));
+    if (st != KVF8_OK) return st;
     hipError_t e = kvf8::launch_kshift(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "kv_shift_rope_per_slot launch");
     return ok();

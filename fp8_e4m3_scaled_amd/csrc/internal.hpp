@@ -26,6 +26,10 @@ struct kvf8_cache {
     std::vector<float> k_scale, v_scale, k_inv, v_inv;
     std::vector<int32_t> free_list;  // LIFO: back() is handed out next
     std::vector<uint8_t> allocated;
+    // checked mode: device state of the index checks (word 0 flags, then one bit per slot)
+    bool checked = false;
+    uint32_t *check_state = nullptr;
+    int64_t check_bitmap_words = 0;
 };
 
 namespace kvf8 {
@@ -119,6 +123,28 @@ hipError_t launch_calibrate(const CalibArgs &a, int32_t sides, void *scales_out,
                             hipStream_t stream);
 
 hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int32_t n_out, hipStream_t stream);
+
+// ---------------------------------------------------------------- checked mode
+constexpr uint32_t kCheckRepeatedSlot = 1u;   // a slot appears twice in one call
+constexpr uint32_t kCheckLength = 2u;         // a length outside its stated bound or the table row
+constexpr uint32_t kCheckBlockId = 4u;        // a used table entry outside [0, num_blocks)
+struct CheckTablesArgs {
+    const int32_t *block_tables;
+    const int32_t *seq_lens;      // decode lengths, or
+    const int32_t *cu_q_lens;     // prefill: chunk offsets [num_seqs + 1] with
+    const int32_t *context_lens;  //   context lengths [num_seqs]
+    int64_t num_blocks;
+    int64_t total_q;
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t block_size;
+    int32_t max_len;              // decode: max_seq_len
+    int32_t max_q_len;            // prefill bounds
+    int32_t max_ctx_len;
+};
+hipError_t launch_check_slots(uint32_t *w, int64_t bitmap_words, const int64_t *slots, int64_t n,
+                              int64_t pool_slots, hipStream_t stream);
+hipError_t launch_check_tables(uint32_t *w, const CheckTablesArgs &a, hipStream_t stream);
 
 struct GatherProbeArgs {
     const uint8_t *k_pool;   // this layer

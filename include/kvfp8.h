@@ -20,8 +20,9 @@
  *     ordinary host memory read before the call returns.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Kernels are enqueued on it and the call returns without waiting.
- *     Only kv_cache_alloc (when it allocates the pools) and kv_cache_free
- *     allocate, set or synchronize device memory; every other call only
+ *     Only kv_cache_alloc (when it allocates the pools), kv_cache_free and
+ *     kv_cache_set_checked allocate, set or synchronize device memory, and
+ *     calls in checked mode wait for their stream; every other call only
  *     launches kernels, so it can be recorded into a HIP graph.
  *   - bf16 tensors are passed as their raw 16-bit patterns (uint16_t).
  *   - A cache handle is not thread-safe; callers serialize calls on one
@@ -150,6 +151,23 @@ kvf8_status kv_cache_elem_types(const kvf8_cache *cache, kvf8_elem *k_elem, kvf8
 
 /* Destroy a cache; frees what kv_cache_alloc allocated.  NULL -> KVF8_OK. */
 kvf8_status kv_cache_free(kvf8_cache *cache);
+
+/*
+ * Checked mode, off by default (a debugging aid for callers that build slot
+ * lists and block tables themselves).  When on, the index inputs the kernels
+ * otherwise take on trust are verified on the device before the real launch,
+ * and a call that fails launches nothing that writes the cache:
+ *   kv_store_fp8, kv_shift_rope, kv_shift_rope_per_slot: a slot that appears
+ *     twice in one call (whose result is otherwise undefined) -> KVF8_E_INVALID;
+ *   paged_attn_decode / paged_attn_prefill_chunk: a length above its stated
+ *     bound (max_seq_len; max_q_len, max_ctx_len, total_q) or past the table
+ *     row, or a table entry in use outside [0, num_blocks) -> KVF8_E_INVALID.
+ * Each check waits for `stream`, so calls in checked mode synchronize and
+ * cannot be recorded into a HIP graph.  Turning it on allocates one bit per
+ * cache slot (plus a word) of device memory on the current device (make the
+ * cache's device current); turning it off frees it.  on: nonzero / zero.
+ */
+kvf8_status kv_cache_set_checked(kvf8_cache *cache, int32_t on);
 
 /* Replace one layer's scales (host values, as in kv_cache_alloc; NULL keeps
  * that side unchanged).  Checked like kv_cache_alloc; on error nothing

@@ -376,3 +376,9 @@ def test_gather_probe_host_checks():
             assert ei.value.status == kv.E_INVALID, args
     finally:
         kv.kv_cache_free(h)
+
+
+def test_checked_mode_needs_a_cache():
+    with pytest.raises(kv.KvF8Error) as ei:
+        kv.kv_cache_set_checked(None, True)
+    assert ei.value.status == kv.E_INVALID
