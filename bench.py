@@ -155,28 +155,17 @@ def run_llama8b(args):
     # one also pays the write-back of the previous fill's dirty lines), then
     # back-to-back decodes.  Timing them interleaved would charge the store's
     # deferred write-back to the decode that follows it.
-    st_ev, de_ev = [], []
     t0 = time.perf_counter()
-    for i in range(args.warmup):
-        store(i)
-    for i in range(args.steps):
-        _time_ms(lambda: store(i), stream, st_ev)
-    torch.cuda.synchronize()
-    for i in range(args.warmup):
-        decode(i)
-    for i in range(args.steps):
-        _time_ms(lambda: decode(i), stream, de_ev)
-    torch.cuda.synchronize()
+    st_t = _timed(store, args.steps, args.warmup, stream)
+    de_t = _timed(decode, args.steps, args.warmup, stream)
     wall = time.perf_counter() - t0
-    st_ms = np.array([s.elapsed_time(e) for s, e in st_ev])
-    de_ms = np.array([s.elapsed_time(e) for s, e in de_ev])
 
     # algorithmic bytes (what the method must move)
     kv_bytes = int(w.total_lengths.sum()) * 2 * w.Hkv * w.D
     blocks = int(sum(-(-int(L) // w.BS) for L in w.total_lengths))
     decode_bytes = kv_bytes + w.B * w.Hq * w.D * (2 + 2) + 4 * blocks + 4 * w.B
     store_bytes = T * (6 * w.Hkv * w.D + 8)
-    de_mean, st_mean = float(de_ms.mean()), float(st_ms.mean())
+    de_mean, st_mean = de_t.mean(), st_t.mean()
     decode_gbps = decode_bytes / (de_mean * 1e-3) / 1e9
     store_gbps = store_bytes / (st_mean * 1e-3) / 1e9
 
@@ -190,7 +179,7 @@ def run_llama8b(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(float((st_ms + de_ms).mean()), 4),
+        "ms_per_step": round(st_mean + de_mean, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -199,14 +188,12 @@ def run_llama8b(args):
         "config": {"workload": "llama8b", "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
                    "block_size": w.BS, "num_seqs": w.B, "seq_len": max_len, "fill_tokens": T,
                    "out_dtype": "bf16", "decode_splits": ws_bytes > 0},
-        "decode": {"ms_mean": round(de_mean, 5), "ms_p10": round(float(np.percentile(de_ms, 10)), 5),
-                   "ms_p50": round(float(np.percentile(de_ms, 50)), 5),
-                   "ms_p90": round(float(np.percentile(de_ms, 90)), 5),
+        "decode": {**_stats(de_t),
                    "algorithmic_bytes": decode_bytes, "GBps": round(decode_gbps, 1),
                    "frac_hbm_peak": round(decode_gbps / HBM_PEAK_GBPS, 4),
                    "tokens_per_s": round(w.B / (de_mean * 1e-3), 1),
                    "kv_tokens_scanned_per_s": round(int(w.total_lengths.sum()) / (de_mean * 1e-3), 1)},
-        "kv_store": {"ms_mean": round(st_mean, 5), "tokens": T, "algorithmic_bytes": store_bytes,
+        "kv_store": {**_stats(st_t), "tokens": T, "algorithmic_bytes": store_bytes,
                      "tokens_per_s": round(T / (st_mean * 1e-3), 1), "GBps": round(store_gbps, 1),
                      "frac_hbm_peak": round(store_gbps / HBM_PEAK_GBPS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(decode_gbps, 1), "peak": HBM_PEAK_GBPS,
@@ -247,13 +234,7 @@ def _calibrate(args, kv, K, V, T, row, ks, vs, stream):
     def call(i):
         kv.kv_calibrate_scales(K, V, row, row, T, row, amax, out, kv.DTYPE_F32, stream)
 
-    for i in range(args.warmup):
-        call(i)
-    ev = []
-    for i in range(args.steps):
-        _time_ms(lambda: call(i), stream, ev)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms = _timed(call, args.steps, args.warmup, stream).mean()
     nbytes = 2 * T * row * 2 + 8 + 8
     got = out.cpu().numpy().view(np.float32)
     return {"ms_mean": round(ms, 5), "algorithmic_bytes": nbytes,
@@ -297,13 +278,7 @@ def _typed_exchange(args, kv, w, K, V, slots_d, T, q, tables, lens, max_len, out
             kv.paged_attn_decode(hs[(i + 1) % 3], 0, q, w.Hq, tables, w.max_blocks, lens, w.B, max_len,
                                  w.sm_scale(), out, kv.DTYPE_BF16, ws, ws_bytes, stream)
 
-        for i in range(args.warmup):
-            decode(i)
-        ev = []
-        for i in range(args.steps):
-            _time_ms(lambda: decode(i), stream, ev)
-        torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        ms = _timed(decode, args.steps, args.warmup, stream).mean()
         nbytes = kv_tokens * w.Hkv * w.D * (keb + veb) + w.B * w.Hq * w.D * 4 + 4 * blocks + 4 * w.B
         res[name] = {"k_elem": "e4m3" if ke == E else "bf16", "v_elem": "e4m3" if ve == E else "bf16",
                      "ms_mean": round(ms, 5), "algorithmic_bytes": nbytes,
@@ -328,13 +303,7 @@ def _gather_ceiling(args, kv, handles, tables, max_blocks, lens, B, Hkv, kv_byte
     def call(i):
         kv.kvf8_gather_probe(handles[(i + 1) % copies], 0, tables, max_blocks, lens, B, out, stream)
 
-    for i in range(args.warmup):
-        call(i)
-    ev = []
-    for i in range(args.steps):
-        _time_ms(lambda: call(i), stream, ev)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms = _timed(call, args.steps, args.warmup, stream).mean()
     gbps = kv_bytes / (ms * 1e-3) / 1e9
     return {"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "ms_mean": round(ms, 5),
             "bytes": kv_bytes, "kernel": "kvf8_gather_probe (one workgroup per (sequence, kv-head))"}
@@ -347,8 +316,8 @@ def _stream_ceiling(kv, stream, nbytes=2 << 30, launches=20):
     bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
     n_out = 1024
     sink = torch.empty(n_out, dtype=torch.int32, device="cuda")
-    ms = _timed(lambda i: kv.kvf8_read_probe(bufs[i % 2], nbytes, sink, n_out, stream), launches, 3, stream)
-    gbps = nbytes / (float(np.median(ms)) * 1e-3) / 1e9
+    ms = _timed(lambda i: kv.kvf8_read_probe(bufs[i % 2], nbytes, sink, n_out, stream), launches, 3, stream).mean()
+    gbps = nbytes / (ms * 1e-3) / 1e9
     del bufs
     return {"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes": nbytes,
             "launches": launches, "kernel": "kvf8_read_probe (XOR-reduce read, 1024 workgroups)"}
@@ -473,8 +442,23 @@ def _fill(w, kv, dev, stream, copies=1, upto=None, empty=False, elems=None):
     return pools, handles
 
 
+class Timing:
+    """Times of `steps` launches of one operation: per-launch HIP-event pairs
+    (for the percentiles) and the mean over one timed region of the same
+    number of back-to-back launches between a single event pair, which has no
+    timing markers between the kernels.  mean() is the region mean."""
+
+    def __init__(self, per_launch, region_ms):
+        self.per_launch = per_launch
+        self.region = float(region_ms)
+
+    def mean(self):
+        return self.region
+
+
 def _timed(fn, steps, warmup, stream):
-    """Per-launch HIP-event times (ms) of fn(i), back to back on `stream`."""
+    """Times of fn(i) on `stream`: warm-up, a phase of per-launch event pairs,
+    a second warm-up, then one event pair around `steps` back-to-back launches."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -482,12 +466,23 @@ def _timed(fn, steps, warmup, stream):
     for i in range(steps):
         _time_ms(lambda: fn(i), stream, ev)
     torch.cuda.synchronize()
-    return np.array([s.elapsed_time(e) for s, e in ev])
+    per = np.array([a.elapsed_time(b) for a, b in ev])
+    for i in range(warmup):
+        fn(i)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(steps):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return Timing(per, a.elapsed_time(b) / steps)
 
 
-def _stats(ms):
-    return {"ms_mean": round(float(ms.mean()), 5), "ms_p10": round(float(np.percentile(ms, 10)), 5),
-            "ms_p50": round(float(np.percentile(ms, 50)), 5), "ms_p90": round(float(np.percentile(ms, 90)), 5)}
+def _stats(t):
+    ms = t.per_launch
+    return {"ms_mean": round(t.mean(), 5), "ms_mean_event_pairs": round(float(ms.mean()), 5),
+            "ms_p10": round(float(np.percentile(ms, 10)), 5), "ms_p50": round(float(np.percentile(ms, 50)), 5),
+            "ms_p90": round(float(np.percentile(ms, 90)), 5)}
 
 
 def _decode_bytes(w, lens, out_bytes):
