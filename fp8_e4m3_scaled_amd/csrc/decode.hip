@@ -76,10 +76,11 @@ struct StepRegs {
 // The all-E4M3 ring issues its loads as inline global_load_dwordx4 and waits
 // for them explicitly (below): the compiler's own wait placement drained
 // every outstanding load at the loop head.  That is only sound while the
-// register allocator neither copies nor spills a ring register between its
-// load and its wait, which a check of the built code confirms for those
-// kernels; the bf16 and mixed-type rings are heavier and use plain loads,
-// whose waits the compiler places itself.
+// register allocator neither copies, reuses nor spills a ring register
+// between its load and its wait.  tests/test_decode_ring_asm.py proves that on
+// the compiled assembly of every all-E4M3 instance (a dataflow pass over the
+// kernel's branches and loop); the bf16 and mixed-type rings are heavier and
+// use plain loads, whose waits the compiler places itself.
 template <int KB, int VB>
 struct AsmRing { static constexpr bool ON = KB == 1 && VB == 1; };
 
@@ -295,6 +296,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     constexpr int KK = D / 32;     // QK^T instructions per tile
     constexpr int MT = D / 16;     // PV instructions per step (one per 16 dims)
     constexpr int NBUF = Depth<D, KB, VB>::NBUF;
+    static_assert(NBUF == 2 || NBUF == 3, "the ring tail below handles up to two remaining steps");
     using Regs = StepRegs<D, KB, VB>;
 
     extern __shared__ float smem[];   // [waves][G] max, [waves][G] sum, [waves][G][D] acc
@@ -375,15 +377,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     // flight (a wave with no steps issues dummy loads of one valid line).
 #pragma unroll
     for (int i = 0; i < NBUF - 1; ++i) issue(buf[i], i);
-    for (int i = 0; i < nsteps; i += NBUF) {
-#pragma clang loop unroll(full)
-        for (int u = 0; u < NBUF; ++u) {
-            const int step = i + u;
-            if (step >= nsteps) break;
-            // keep the next NBUF-1 steps' loads in flight while this one computes
-            issue(buf[(u + NBUF - 1) % NBUF], step + NBUF - 1);
-            wait_step<LOADS * (NBUF - 1)>(buf[u]);
-            compute_step<D, KB, VB>(st, buf[u], qb, p0 + step * stride, c1, g, a.qk_scale);
+    // Full rounds of NBUF steps, then the remaining steps (fewer than NBUF)
+    // in nested branches: the loop has one exit, and a skipped step skips
+    // every later one, so each path through the code is one the ring can take.
+    auto step_at = [&](int step, int u) {
+        // keep the next NBUF-1 steps' loads in flight while this one computes
+        issue(buf[(u + NBUF - 1) % NBUF], step + NBUF - 1);
+        wait_step<LOADS * (NBUF - 1)>(buf[u]);
+        compute_step<D, KB, VB>(st, buf[u], qb, p0 + step * stride, c1, g, a.qk_scale);
+    };
+    const int full = nsteps - nsteps % NBUF;
+    for (int i = 0; i < full; i += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) step_at(i + u, u);
+    }
+    const int rest = nsteps - full;
+    if (rest > 0) {
+        step_at(full, 0);
+        if constexpr (NBUF > 2) {
+            if (rest > 1) step_at(full + 1, 1);
         }
     }
     // Drain the ring.  The wait names every ring register, so none of them can

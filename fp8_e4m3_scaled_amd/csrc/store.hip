@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a) {
     const int runs = D >> 4;            // 16-dim runs per head
     const int quads = D >> 2;           // 4-dim runs per head
     const int k_items = 4 * H * runs;   // per group: 4 tokens x H heads x runs
-    const int v_items = H * quads;      // per group (four-token path)
+    const int v_items = H * quads;      // per group: H heads x quads, each over the four tokens
 
 #pragma unroll
     for (int grp = 0; grp < kGroups; ++grp) {
@@ -56,16 +56,21 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a) {
             if (slot[k] >= a.pool_slots) slot[k] = -1;    // outside the pool: skipped, never written
         }
 
+        // Every data load below depends only on the token count, not on the
+        // slots, so the slot reads and the K/V reads are in flight together;
+        // the slots only decide where (and whether) the results are written.
+
         // ---------------- K: 16 dims of one token -> one 16-byte run of codes
         for (int it = threadIdx.x; it < k_items; it += kStoreThreads) {
             const int k = it / (H * runs);
             const int rem = it - k * (H * runs);
             const int h = rem / runs;
             const int r = rem - h * runs;
-            const int64_t s = slot[k];
-            if (s < 0) continue;
+            if (tok0 + k >= a.num_tokens) continue;
             const u32x4 *src = reinterpret_cast<const u32x4 *>(kin + (tok0 + k) * a.k_stride + (int64_t)h * D + r * 16);
             const u32x4 lo = src[0], hi = src[1];
+            const int64_t s = slot[k];
+            if (s < 0) continue;
             const int64_t blk = s / BS;
             const int t = (int)(s - blk * BS);
             const int d0 = r * 16;
@@ -87,26 +92,27 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a) {
             }
         }
 
-        // ---------------- V
+        // ---------------- V: an item is four dims of the four tokens
         const bool group = slot[0] >= 0 && (slot[0] & 3) == 0 && slot[1] == slot[0] + 1 &&
                            slot[2] == slot[0] + 2 && slot[3] == slot[0] + 3;
-        if (group) {
-            // four dims x four tokens -> one 16-byte run of codes
-            const int64_t blk = slot[0] / BS;
-            const int t0 = (int)(slot[0] - blk * BS);
-            for (int it = threadIdx.x; it < v_items; it += kStoreThreads) {
-                const int h = it / quads;
-                const int d4 = it - h * quads;
-                uint32_t b[4][4];   // [token][dim] bf16 bits
+        for (int it = threadIdx.x; it < v_items; it += kStoreThreads) {
+            const int h = it / quads;
+            const int d4 = it - h * quads;
+            uint32_t b[4][4];   // [token][dim] bf16 bits
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint2 w = *reinterpret_cast<const uint2 *>(vin + (tok0 + k) * a.v_stride +
-                                                                     (int64_t)h * D + d4 * 4);
-                    b[k][0] = w.x & 0xFFFF;
-                    b[k][1] = w.x >> 16;
-                    b[k][2] = w.y & 0xFFFF;
-                    b[k][3] = w.y >> 16;
-                }
+            for (int k = 0; k < 4; ++k) {
+                uint2 w = make_uint2(0u, 0u);
+                if (tok0 + k < a.num_tokens)
+                    w = *reinterpret_cast<const uint2 *>(vin + (tok0 + k) * a.v_stride + (int64_t)h * D + d4 * 4);
+                b[k][0] = w.x & 0xFFFF;
+                b[k][1] = w.x >> 16;
+                b[k][2] = w.y & 0xFFFF;
+                b[k][3] = w.y >> 16;
+            }
+            if (group) {
+                // the four tokens fill one aligned 4-token group: 16 consecutive codes
+                const int64_t blk = slot[0] / BS;
+                const int t0 = (int)(slot[0] - blk * BS);
                 const int64_t off = (blk * H + h) * tile + ((int64_t)(t0 >> 2) * D + d4 * 4) * 4;
                 if constexpr (VB == 1) {
                     u32x4 out;
@@ -129,35 +135,30 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a) {
                     dst[0] = o0;
                     dst[1] = o1;
                 }
-            }
-        } else {
-            // one token at a time: its four codes sit 4 bytes apart
-            for (int it = threadIdx.x; it < 4 * v_items; it += kStoreThreads) {
-                const int k = it / v_items;
-                const int rem = it - k * v_items;
-                const int h = rem / quads;
-                const int d4 = rem - h * quads;
-                const int64_t s = slot[k];
-                if (s < 0) continue;
-                const uint2 w = *reinterpret_cast<const uint2 *>(vin + (tok0 + k) * a.v_stride +
-                                                                 (int64_t)h * D + d4 * 4);
-                const int64_t blk = s / BS;
-                const int t = (int)(s - blk * BS);
-                const int64_t e = (blk * H + h) * tile + ((int64_t)(t >> 2) * D + d4 * 4) * 4 + (t & 3);
-                if constexpr (VB == 1) {
-                    const uint32_t c = encode4(scaled(w.x & 0xFFFF, a.v_inv), scaled(w.x >> 16, a.v_inv),
-                                               scaled(w.y & 0xFFFF, a.v_inv), scaled(w.y >> 16, a.v_inv));
-                    uint8_t *dst = vout + e;
-                    dst[0] = (uint8_t)(c & 0xFF);
-                    dst[4] = (uint8_t)((c >> 8) & 0xFF);
-                    dst[8] = (uint8_t)((c >> 16) & 0xFF);
-                    dst[12] = (uint8_t)(c >> 24);
-                } else {
-                    uint16_t *dst = reinterpret_cast<uint16_t *>(vout) + e;
-                    dst[0] = (uint16_t)(w.x & 0xFFFF);
-                    dst[4] = (uint16_t)(w.x >> 16);
-                    dst[8] = (uint16_t)(w.y & 0xFFFF);
-                    dst[12] = (uint16_t)(w.y >> 16);
+            } else {
+                // token by token: a token's four codes sit 4 bytes apart
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int64_t s = slot[k];
+                    if (s < 0) continue;
+                    const int64_t blk = s / BS;
+                    const int t = (int)(s - blk * BS);
+                    const int64_t e = (blk * H + h) * tile + ((int64_t)(t >> 2) * D + d4 * 4) * 4 + (t & 3);
+                    if constexpr (VB == 1) {
+                        const uint32_t c = encode4(scaled(b[k][0], a.v_inv), scaled(b[k][1], a.v_inv),
+                                                   scaled(b[k][2], a.v_inv), scaled(b[k][3], a.v_inv));
+                        uint8_t *dst = vout + e;
+                        dst[0] = (uint8_t)(c & 0xFF);
+                        dst[4] = (uint8_t)((c >> 8) & 0xFF);
+                        dst[8] = (uint8_t)((c >> 16) & 0xFF);
+                        dst[12] = (uint8_t)(c >> 24);
+                    } else {
+                        uint16_t *dst = reinterpret_cast<uint16_t *>(vout) + e;
+                        dst[0] = (uint16_t)b[k][0];
+                        dst[4] = (uint16_t)b[k][1];
+                        dst[8] = (uint16_t)b[k][2];
+                        dst[12] = (uint16_t)b[k][3];
+                    }
                 }
             }
         }
