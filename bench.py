@@ -543,9 +543,11 @@ def run_prefill(args):
     res["kv_store"] = dict(_stats(st), tokens=T, algorithmic_bytes=store_bytes,
                            tokens_per_s=round(T / (st.mean() * 1e-3), 1),
                            GBps=round(store_bytes / (st.mean() * 1e-3) / 1e9, 1))
+    psha = _source_sha("prefill.hip", "fp8_device.hpp", "internal.hpp")
     res["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                        "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                       "traffic": None, "kernel": "prefill_kernel<128,16>"}
+                       "traffic": _traffic_from_profile("prefill_pmc.txt", psha),
+                       "kernel": "prefill_kernel<128,16,1,1>", "kernel_source_sha": psha}
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = _cpu_prefill(w, q, out, ctx, n, args.cpu_seconds)
     kv.kv_cache_free(h)
@@ -684,9 +686,11 @@ def run_longctx(args):
     res["kv_shift_per_slot"] = dict(_stats(sp), algorithmic_bytes=sp_bytes, GBps=round(sp_gbps, 1),
                                     frac_hbm_peak=round(sp_gbps / HBM_PEAK_GBPS, 4), distinct_deltas=w.B,
                                     tokens_per_s=round(nsl / (sp.mean() * 1e-3), 1))
+    dsha = _source_sha("decode.hip", "fp8_device.hpp", "decode_args.hpp")
     res["roofline"] = {"bound": "hbm", "achieved": round(de_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                       "frac": round(de_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                       "kernel": "decode_kernel<256,32,1,1> + decode_reduce<256>"}
+                       "frac": round(de_gbps / HBM_PEAK_GBPS, 4),
+                       "traffic": _traffic_from_profile("decode_longctx_pmc.txt", dsha),
+                       "kernel": "decode_kernel<256,32,1,1> + decode_reduce<256>", "kernel_source_sha": dsha}
     for h in handles:
         kv.kv_cache_free(h)
     return res
@@ -738,9 +742,11 @@ def run_varlen(args):
                          frac_hbm_peak=round(de_gbps / HBM_PEAK_GBPS, 4),
                          tokens_per_s=round(w.B / (de.mean() * 1e-3), 1))
     res["kv_store"] = dict(_stats(st), tokens=w.B, tokens_per_s=round(w.B / (st.mean() * 1e-3), 1))
+    dsha = _source_sha("decode.hip", "fp8_device.hpp", "decode_args.hpp")
     res["roofline"] = {"bound": "hbm", "achieved": round(de_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                       "frac": round(de_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                       "kernel": "decode_kernel<128,16,1,1> + decode_reduce<128>"}
+                       "frac": round(de_gbps / HBM_PEAK_GBPS, 4),
+                       "traffic": _traffic_from_profile("decode_varlen_pmc.txt", dsha),
+                       "kernel": "decode_kernel<128,16,1,1> + decode_reduce<128>", "kernel_source_sha": dsha}
     # Beside the linear-stream ceiling: a plain read of the same tiles with one
     # workgroup per (sequence, kv-head) and no split, which the decode's split
     # plan beats on this length mix (long sequences would serialize).
