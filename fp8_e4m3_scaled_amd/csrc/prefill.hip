@@ -86,16 +86,24 @@ __device__ __forceinline__ void load_to_lds16(const void *src, uint8_t *wave_dst
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)wave_dst, 16, 0, 0);
 }
 
+// Maximum of raw scores with the NaN-propagating v_maximum(3)_f32: fmaxf in
+// IEEE mode first quiets each operand that is not known to be canonical (every
+// MFMA result and every lane-swapped value), one extra VALU op per value.  A
+// NaN score makes its row's maximum NaN, which only keeps that step from
+// moving the reference (a NaN comparison is false); the row's output is NaN
+// either way, through that key's probability.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // max(v, v of lane ^ 16) and max(v, v of lane ^ 32) with the gfx950 row
 // swaps (full-rate VALU, no LDS round trip): with both operands the same
 // register, each lane gets back its own value and its partner's.
 __device__ __forceinline__ float max_xor16(float v) {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_xor32(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Wait until at most N of this wave's vector-memory loads are outstanding.
@@ -317,20 +325,28 @@ void prefill_kernel(PrefillArgs a) {
     // A lane's CH chunks sit at fixed offsets inside their block's tile:
     // steps start on 32-key boundaries and BS divides 32, so a tile's first
     // in-block key is 16t mod BS at every step and only the block ids change.
-    const uint8_t *csrc[CH];
-    int64_t cstride[CH];
-    int cdst[CH];
-    bool cone[CH];
+    // Chunks are wave-aligned (TOTAL and kThreads are multiples of 64), so a
+    // chunk's pool, tile and LDS destination are the same for the whole wave:
+    // they are kept as scalars, and each step's source is a scalar block base
+    // plus the lane's fixed 32-bit offset (the scalar-base form of the load),
+    // with no per-lane address arithmetic in the loop.
+    uint32_t coff[CH];          // per lane: byte offset from the chunk's block base
+    const uint8_t *cpool[CH];   // per wave: K or V pool
+    int64_t cstride[CH];        // per wave: bytes per pool block
+    int cdst[CH];               // per wave: LDS byte offset inside a stage
+    int cone[CH];               // per wave: the step's second 16-key tile
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
         int c = threadIdx.x + i * kThreads;
         if (c >= TOTAL) c -= kThreads;                  // whole waves: repeat the previous chunk
         constexpr int KPT = KTILE / 16, VPT = VTILE / 16;
-        const bool is_k = c < 2 * KPT;
-        csrc[i] = chunk_src<D, BS, KB, VB>(c, a.k_pool, a.v_pool, 0u, 0u, a.kv_heads, kvh, 0);
+        const int is_k = __builtin_amdgcn_readfirstlane(c < 2 * KPT ? 1 : 0);
+        cpool[i] = is_k ? a.k_pool : a.v_pool;
+        coff[i] = (uint32_t)(chunk_src<D, BS, KB, VB>(c, a.k_pool, a.v_pool, 0u, 0u, a.kv_heads, kvh, 0) -
+                             cpool[i]);
         cstride[i] = (int64_t)a.kv_heads * BS * D * (is_k ? KB : VB);
-        cone[i] = (is_k ? c / KPT : (c - 2 * KPT) / VPT) == 1;
-        cdst[i] = (c - lane) * 16;
+        cone[i] = __builtin_amdgcn_readfirstlane((is_k ? c / KPT : (c - 2 * KPT) / VPT) == 1 ? 1 : 0);
+        cdst[i] = __builtin_amdgcn_readfirstlane((c - lane) * 16);
     }
     auto issue = [&](int st) {
         const int p = st * kStep;
@@ -338,8 +354,14 @@ void prefill_kernel(PrefillArgs a) {
         blocks_of(p, b0, b1);
         uint8_t *stage = lds[st % kStages];
 #pragma unroll
-        for (int i = 0; i < CH; ++i)
-            load_to_lds16(csrc[i] + (int64_t)(cone[i] ? b1 : b0) * cstride[i], stage + cdst[i]);
+        for (int i = 0; i < CH; ++i) {
+            // the block base stays one scalar value (readfirstlane keeps the
+            // compiler from folding it into a per-lane 64-bit multiply-add)
+            const uint64_t bu = (uint64_t)(cpool[i] + (int64_t)(cone[i] ? b1 : b0) * cstride[i]);
+            const uint64_t bs = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bu >> 32)) << 32) |
+                                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bu);
+            load_to_lds16(reinterpret_cast<const uint8_t *>(bs) + coff[i], stage + cdst[i]);
+        }
     };
 
 #pragma unroll
@@ -420,8 +442,9 @@ void prefill_kernel(PrefillArgs a) {
                         if (key > row_pos[j] || key >= total) x[j][4 * t + i] = -__builtin_inff();
                     }
             }
-            float m8 = fmaxf(fmaxf(fmaxf(x[j][0], x[j][1]), fmaxf(x[j][2], x[j][3])),
-                             fmaxf(fmaxf(x[j][4], x[j][5]), fmaxf(x[j][6], x[j][7])));
+            float m8 = vmax(vmax(vmax(x[j][0], x[j][1]), x[j][2]),
+                            vmax(vmax(x[j][3], x[j][4]), x[j][5]));
+            m8 = vmax(vmax(m8, x[j][6]), x[j][7]);
             m8 = max_xor16(m8);            // the row's four k-groups: lanes n, n^16, n^32, n^48
             m8 = max_xor32(m8);
             mx[j] = m8 * qk_row[j];
