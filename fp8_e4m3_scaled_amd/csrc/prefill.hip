@@ -295,15 +295,21 @@ void prefill_kernel(PrefillArgs a) {
 
     // run_max starts at a finite sentinel far below any score, so that
     // exp2(s*qk - run_max) of a masked score (-inf) is 0 without a select and
-    // the first rescale factor exp2(sentinel - ref) is 0.  run_sum holds this
-    // lane's share of the row sum (its four k-groups are added at the end).
+    // the first rescale factor exp2(sentinel - ref) is 0.  With E4M3 V the
+    // row sums come from the matrix cores: one more product per row tile and
+    // step, of an all-ones operand with the same f16 P as the P.V product, so
+    // every element of rsum[j] holds the whole row's sum of the P it used.
+    // With bf16 V, run_sum holds this lane's share of the row sum (its four
+    // k-groups are added at the end).
     f32x4 acc[kNR][MT];
+    f32x4 rsum[kNR];
     float run_sum[kNR];
     float run_max[kNR];
 #pragma unroll
     for (int j = 0; j < kNR; ++j) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        rsum[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         run_sum[j] = 0.0f;
         run_max[j] = kNoMax;
     }
@@ -455,7 +461,10 @@ void prefill_kernel(PrefillArgs a) {
             for (int j = 0; j < kNR; ++j) {
                 const float ref = fmaxf(run_max[j], mx[j]);
                 const float alpha = __builtin_amdgcn_exp2f(run_max[j] - ref);
-                run_sum[j] *= alpha;
+                if constexpr (VB == 1)
+                    rsum[j] *= alpha;
+                else
+                    run_sum[j] *= alpha;
 #pragma unroll
                 for (int t = 0; t < MT; ++t) acc[j][t] *= alpha;
                 run_max[j] = ref;
@@ -482,10 +491,12 @@ void prefill_kernel(PrefillArgs a) {
                 pb[j] = f16x8{(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3],
                               (_Float16)pr[4], (_Float16)pr[5], (_Float16)pr[6], (_Float16)pr[7]};
             }
-            float ps = 0.0f;
+            if constexpr (VB == 2) {
+                float ps = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ps += pr[i];
-            run_sum[j] += ps;
+                for (int i = 0; i < 8; ++i) ps += pr[i];
+                run_sum[j] += ps;
+            }
         }
         // ---- O^T += V^T P^T, V operands read now and converted once for
         // both row tiles (lane (m, g) holds keys 4g..4g+3 of dims (D/16)m..)
@@ -554,6 +565,11 @@ void prefill_kernel(PrefillArgs a) {
                 for (int j = 0; j < kNR; ++j)
                     acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[j], acc[j][t], 0, 0, 0);
             }
+            const _Float16 one = (_Float16)1.0f;
+            const f16x8 ones = {one, one, one, one, one, one, one, one};
+#pragma unroll
+            for (int j = 0; j < kNR; ++j)
+                rsum[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[j], rsum[j], 0, 0, 0);
         }
     }
     wait_vmcnt<0>();    // no LDS write may still be in flight when the workgroup ends
@@ -561,9 +577,14 @@ void prefill_kernel(PrefillArgs a) {
     // ---- normalize and write: lane (n, g) holds rows n of its tiles, dims (D/16)(4g+r)+t
 #pragma unroll
     for (int j = 0; j < kNR; ++j) {
-        float l = run_sum[j];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        float l;
+        if constexpr (VB == 1) {
+            l = rsum[j][0];
+        } else {
+            l = run_sum[j];
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+        }
         if (!row_live[j]) continue;
         const int r = (wave * kNR + j) * 16 + m;
         const int tok = i0 + r / G;
