@@ -168,7 +168,9 @@ void prefill_kernel(PrefillArgs a) {
     const uint32_t hid = blockIdx.x;
     const uint32_t kx = hid >> 3;
     const int pair = (int)(kx / (uint32_t)a.q_tiles) * 8 + (int)(hid & 7);
-    const int qt = (int)(kx % (uint32_t)a.q_tiles);
+    // a pair's tiles go out longest first (the last query tile sees the most
+    // keys), so the shorter ones fill in behind them at the end of the grid
+    const int qt = a.q_tiles - 1 - (int)(kx % (uint32_t)a.q_tiles);
     if (pair >= a.num_seqs * a.kv_heads) return;
     const int kvh = pair % a.kv_heads;
     const int b = pair / a.kv_heads;
