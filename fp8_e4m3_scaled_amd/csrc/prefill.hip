@@ -450,18 +450,23 @@ void prefill_kernel(PrefillArgs a) {
                         if (key > row_pos[j] || key >= total) x[j][4 * t + i] = -__builtin_inff();
                     }
             }
+            // This lane's maximum over its 8 keys of the row.  The row's maximum
+            // passes the bound exactly when one of its four lanes' does (the bound
+            // is the same in all four and the scaling is monotonic), so the vote
+            // needs no cross-lane step; the row maximum itself is only formed in
+            // the rescale branch.
             float m8 = vmax(vmax(vmax(x[j][0], x[j][1]), x[j][2]),
                             vmax(vmax(x[j][3], x[j][4]), x[j][5]));
             m8 = vmax(vmax(m8, x[j][6]), x[j][7]);
-            m8 = max_xor16(m8);            // the row's four k-groups: lanes n, n^16, n^32, n^48
-            m8 = max_xor32(m8);
-            mx[j] = m8 * qk_row[j];
-            grow |= mx[j] > run_max[j] + kLazy;
+            mx[j] = m8;
+            grow |= m8 * qk_row[j] > run_max[j] + kLazy;
         }
         if (__any(grow)) {
 #pragma unroll
             for (int j = 0; j < kNR; ++j) {
-                const float ref = fmaxf(run_max[j], mx[j]);
+                // the row's four k-groups: lanes n, n^16, n^32, n^48
+                const float row_max = max_xor32(max_xor16(mx[j])) * qk_row[j];
+                const float ref = fmaxf(run_max[j], row_max);
                 const float alpha = __builtin_amdgcn_exp2f(run_max[j] - ref);
                 if constexpr (VB == 1)
                     rsum[j] *= alpha;
