@@ -206,26 +206,40 @@ __global__ __launch_bounds__(kThreads) void kshift_slot_runs(KShiftArgs a, int r
     const int bs_log2 = a.block_size == 32 ? 5 : 4;
     const int runs = NEOX ? a.rot_dim / 32 : a.rot_dim / 16;
     const int half = a.rot_dim / 2;
-    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int r = (int)(g & ((1 << rp_log2) - 1));
+    const int lane = threadIdx.x & 63;
+    const int r = lane & ((1 << rp_log2) - 1);
     if (r >= runs) return;
-    const int64_t sstep = ((int64_t)gridDim.x * kThreads) >> rp_log2;
+    // Each wave walks one contiguous span of the slot list, 64 / RP slots per
+    // iteration (its lanes cover those slots' runs, so accesses stay as
+    // coalesced as a grid stride).  A lane's successive slots are then close in
+    // the list, where neighbouring slots usually share a delta: the lane keeps
+    // its row's cos/sin (widened to fp64) until the row index changes.
+    const int spw = 64 >> rp_log2;
+    const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+    const int64_t wave_id = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+    const int64_t per_wave = (a.n_slots + nwaves - 1) / nwaves;
+    const int64_t span = (per_wave + spw - 1) / spw * spw;
+    const int64_t s_end = min(a.n_slots, (wave_id + 1) * span);
     const int p0 = NEOX ? 16 * r : 8 * r;
     const int da = 16 * r;
     const int db = da + half;
-    for (int64_t si = g >> rp_log2; si < a.n_slots; si += sstep) {
+    double cs[NP], sn[NP];
+    int32_t cached = -1;
+    for (int64_t si = wave_id * span + (lane >> rp_log2); si < s_end; si += spw) {
         const int64_t slot = a.slots[si];
         const int32_t row = a.rows[si];
         if (slot < 0 || slot >= a.pool_slots || row < 0 || row >= a.n_rows) continue;
-        const f32x4 *tp = reinterpret_cast<const f32x4 *>(a.table + ((int64_t)row * half + p0) * 2);
-        double cs[NP], sn[NP];
+        if (row != cached) {
+            const f32x4 *tp = reinterpret_cast<const f32x4 *>(a.table + ((int64_t)row * half + p0) * 2);
 #pragma unroll
-        for (int k = 0; k < NP / 2; ++k) {
-            const f32x4 v = tp[k];
-            cs[2 * k] = (double)v[0];
-            sn[2 * k] = (double)v[1];
-            cs[2 * k + 1] = (double)v[2];
-            sn[2 * k + 1] = (double)v[3];
+            for (int k = 0; k < NP / 2; ++k) {
+                const f32x4 v = tp[k];
+                cs[2 * k] = (double)v[0];
+                sn[2 * k] = (double)v[1];
+                cs[2 * k + 1] = (double)v[2];
+                sn[2 * k + 1] = (double)v[3];
+            }
+            cached = row;
         }
         const int64_t blk = slot >> bs_log2;
         const int t = (int)(slot - (blk << bs_log2));
