@@ -336,8 +336,8 @@ void prefill_kernel(PrefillArgs a) {
     // Chunks are wave-aligned (TOTAL and kThreads are multiples of 64), so a
     // chunk's pool, tile and LDS destination are the same for the whole wave:
     // they are kept as scalars, and each step's source is a scalar block base
-    // plus the lane's fixed 32-bit offset (the scalar-base form of the load),
-    // with no per-lane address arithmetic in the loop.
+    // plus the lane's fixed 32-bit offset: one 64-bit add per chunk and step is
+    // the only per-lane address arithmetic in the loop.
     uint32_t coff[CH];          // per lane: byte offset from the chunk's block base
     const uint8_t *cpool[CH];   // per wave: K or V pool
     int64_t cstride[CH];        // per wave: bytes per pool block
