@@ -194,9 +194,10 @@ __global__ __launch_bounds__(kThreads) void kshift_runs(KShiftArgs a, int rp_log
 }
 
 // Per-slot path, runs.  Every slot carries its own row of the cos/sin table
-// (a.rows[si] into a.table, [row][pair][cos, sin] fp32).  Thread g works on
-// run r = g mod RP of slots g / RP, g / RP + J, ...; for each slot it loads its
-// run's cos/sin once (16-byte loads of the interleaved row) and rotates that
+// (a.rows[si] into a.table, [row][pair][cos, sin] fp32).  Lane l of a wave
+// works on run r = l mod RP of the wave's span of slots, 64 / RP slots per
+// iteration; it loads its run's cos/sin (16-byte loads of the interleaved row)
+// only when the slot's row differs from the previous slot's, and rotates that
 // run in every kv-head, one head after the other (two heads in flight, or
 // (slot, head) items with a table load each, measured slower).
 template <bool NEOX>
