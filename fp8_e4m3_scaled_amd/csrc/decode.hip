@@ -84,12 +84,32 @@ struct StepRegs {
 template <int KB, int VB>
 struct AsmRing { static constexpr bool ON = KB == 1 && VB == 1; };
 
-template <bool ASM>
-__device__ __forceinline__ void gload16(u32x4 &dst, const void *p) {
+// 16 bytes at p + OFF (OFF an immediate of the instruction).
+template <bool ASM, int OFF>
+__device__ __forceinline__ void gload16(u32x4 &dst, const uint8_t *p) {
     if constexpr (ASM)
-        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst) : "v"(p) : "memory");
+        asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(dst) : "v"(p), "n"(OFF) : "memory");
     else
-        dst = *reinterpret_cast<const u32x4 *>(p);
+        dst = *reinterpret_cast<const u32x4 *>(p + OFF);
+}
+
+// N consecutive 16-byte loads at p + 16*I, I = 0..N-1 (immediate offsets).
+template <bool ASM, int I, int N>
+struct LoadRun {
+    static __device__ __forceinline__ void run(u32x4 *dst, const uint8_t *p) {
+        if constexpr (I < N) {
+            gload16<ASM, 16 * I>(dst[I], p);
+            LoadRun<ASM, I + 1, N>::run(dst, p);
+        }
+    }
+};
+
+// A 64-bit address that is the same in every lane, kept as one scalar value
+// (so that the per-lane part of a load address is a single add).
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+    const uint64_t u = (uint64_t)p;
+    return reinterpret_cast<const uint8_t *>(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32)) << 32) |
+                                             (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u));
 }
 
 // Wait until at most N vector-memory loads are outstanding, then hand the
@@ -111,13 +131,17 @@ __device__ __forceinline__ void wait_step(StepRegs<D, KB, VB> &r) {
 // Issue the loads of one 32-token step: per lane, for each of the two
 // 16-token tiles, the D/4 elements of key m in column quarter g (K) and keys
 // 4g..4g+3 of dims (D/16)m.. (V), as 16-byte loads.  blk0 / blk1 are the
-// pool blocks of the two tiles.  A step past the wave's end (live == false)
-// keeps the same number of loads but points every lane at one shared 16-byte
-// line, so the ring stays branch-free without moving extra bytes.
+// pool blocks of the two tiles.  A tile's base (block, kv-head and first
+// in-block key) is the same for the whole wave and is formed as a scalar; the
+// lane adds its fixed offsets koff / voff ((g*BS + m)*D/4 and
+// (g*D + (D/16)m)*4 elements), and the 16-byte pieces are immediate offsets
+// of the loads.  A step past the wave's end (live == false) keeps the same
+// number of loads but reads the first bytes of the K pool, so the ring stays
+// branch-free without moving extra bytes.
 template <int D, int BS, int KB, int VB>
 __device__ __forceinline__ void load_step(StepRegs<D, KB, VB> &r, const uint8_t *k_pool, const uint8_t *v_pool,
                                           uint32_t blk0, uint32_t blk1, int kv_heads, int kvh, int p,
-                                          int m, int g, bool live) {
+                                          uint32_t koff, uint32_t voff, bool live) {
     constexpr int Q4 = D / 4;
     using R = StepRegs<D, KB, VB>;
 #pragma unroll
@@ -125,14 +149,12 @@ __device__ __forceinline__ void load_step(StepRegs<D, KB, VB> &r, const uint8_t 
         const uint32_t blk = t == 0 ? blk0 : blk1;
         const int tb = (p + 16 * t) % BS;
         const int64_t tile = ((int64_t)blk * kv_heads + kvh) * (BS * D);     // element index of the tile
-        const uint8_t *kp = live ? k_pool + (tile + (int64_t)(g * BS + tb + m) * Q4) * KB : k_pool;
-        const uint8_t *vp = live ? v_pool + (tile + (int64_t)((tb / 4 + g) * D + (D / 16) * m) * 4) * VB
-                                 : k_pool;
-        const int inc = live ? 16 : 0;
-#pragma unroll
-        for (int i = 0; i < R::NK; ++i) gload16<AsmRing<KB, VB>::ON>(r.k[t][i], kp + inc * i);
-#pragma unroll
-        for (int i = 0; i < R::NV; ++i) gload16<AsmRing<KB, VB>::ON>(r.v[t][i], vp + inc * i);
+        const uint8_t *kb = uniform_ptr(live ? k_pool + (tile + (int64_t)tb * Q4) * KB : k_pool);
+        const uint8_t *vb = uniform_ptr(live ? v_pool + (tile + (int64_t)(tb / 4) * D * 4) * VB : k_pool);
+        const uint8_t *kp = kb + (live ? koff : 0u);
+        const uint8_t *vp = vb + (live ? voff : 0u);
+        LoadRun<AsmRing<KB, VB>::ON, 0, R::NK>::run(r.k[t], kp);
+        LoadRun<AsmRing<KB, VB>::ON, 0, R::NV>::run(r.v[t], vp);
     }
 }
 
@@ -365,12 +387,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int nsteps = c1 > c0 + kStep * wave ? (c1 - c0 - kStep * wave + stride - 1) / stride : 0;
     const int p0 = c0 + kStep * wave;
     constexpr int LOADS = 2 * (Regs::NK + Regs::NV);   // loads per step
+    // this lane's fixed byte offsets inside a K tile half and a V tile half
+    const uint32_t koff = (uint32_t)((g * BS + m) * (D / 4) * KB);
+    const uint32_t voff = (uint32_t)((g * D + (D / 16) * m) * 4 * VB);
     auto issue = [&](Regs &r, int i) {
         const bool live = i < nsteps;
         const int ii = live ? i : 0;
         const uint32_t b0 = __builtin_amdgcn_readlane(ids, 2 * ii);
         const uint32_t b1 = __builtin_amdgcn_readlane(ids, 2 * ii + 1);
-        load_step<D, BS, KB, VB>(r, a.k_pool, a.v_pool, b0, b1, a.kv_heads, kvh, p0 + ii * stride, m, g, live);
+        load_step<D, BS, KB, VB>(r, a.k_pool, a.v_pool, b0, b1, a.kv_heads, kvh, p0 + ii * stride, koff, voff, live);
     };
     Regs buf[NBUF];
     // Unconditional, so that every path into the loop holds the same loads in
