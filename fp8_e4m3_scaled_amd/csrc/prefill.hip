@@ -384,6 +384,7 @@ void prefill_kernel(PrefillArgs a) {
         // also wait for the transfers still in flight.  The ds_reads of step
         // s-1 were consumed by its MFMAs, so none is pending here.
         asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_s_setprio(0);
         issue(s + kStages - 1);
 
         const bool diag = p + kStep > first_row_pos;      // some key may be past some row
@@ -505,6 +506,11 @@ void prefill_kernel(PrefillArgs a) {
                 run_sum[j] += ps;
             }
         }
+        // A wave that reaches its P.V products runs them at raised priority, so
+        // that the SIMD's other waves fill the matrix cores' shadow with their
+        // softmax work rather than the other way round (~2.5 %); the priority
+        // drops back after the next step's barrier.
+        __builtin_amdgcn_s_setprio(1);
         // ---- O^T += V^T P^T, V operands read now and converted once for
         // both row tiles (lane (m, g) holds keys 4g..4g+3 of dims (D/16)m..)
         if constexpr (VB == 2) {
@@ -579,6 +585,7 @@ void prefill_kernel(PrefillArgs a) {
                 rsum[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[j], rsum[j], 0, 0, 0);
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     wait_vmcnt<0>();    // no LDS write may still be in flight when the workgroup ends
 
     // ---- normalize and write: lane (n, g) holds rows n of its tiles, dims (D/16)(4g+r)+t
