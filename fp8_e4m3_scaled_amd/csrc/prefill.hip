@@ -60,6 +60,20 @@ struct StepLds {
     static constexpr int BYTES = 2 * (KTILE + VTILE);
 };
 
+// LDS image swizzle.  A lane reads PP consecutive 16-byte pieces of its key
+// (K) or key group (V) at a stride of PP pieces between neighbouring lanes, so
+// lanes m and m + 16/PP would hit the same banks.  Inside every aligned group
+// of 16 pieces the image stores piece q at position q ^ ((q >> 4) & (PP - 1))
+// (a permutation of the group, its own inverse): a lane's pieces then start
+// at a lane-dependent rotation and the reads spread over all banks.  The copy
+// fetches the same 16-piece groups, so every copy instruction still reads the
+// same contiguous global bytes, only in another lane order.
+template <int D, int EB>
+struct Swz {
+    static constexpr int PP = D * EB / 64;              // 16-byte pieces per lane per tile
+    static __device__ __forceinline__ int pos(int q) { return PP > 1 ? q ^ ((q >> 4) & (PP - 1)) : q; }
+};
+
 // Per-thread share of one step's global->LDS copy: 16-byte chunks, rounded up
 // (a lane without a last chunk repeats its previous one, so that every lane
 // issues the same number of loads and the vmcnt arithmetic holds).
@@ -350,12 +364,19 @@ void prefill_kernel(PrefillArgs a) {
         constexpr int KPT = KTILE / 16, VPT = VTILE / 16;
         const int is_k = __builtin_amdgcn_readfirstlane(c < 2 * KPT ? 1 : 0);
         cpool[i] = is_k ? a.k_pool : a.v_pool;
-        coff[i] = (uint32_t)(chunk_src<D, BS, KB, VB>(c, a.k_pool, a.v_pool, 0u, 0u, a.kv_heads, kvh, 0) -
+        // LDS position c holds image piece Swz::pos(c) of its tile (positions
+        // and pieces are counted from the step image's start; tiles are whole
+        // 16-piece groups)
+        const int piece = is_k ? Swz<D, KB>::pos(c) : 2 * KPT + Swz<D, VB>::pos(c - 2 * KPT);
+        coff[i] = (uint32_t)(chunk_src<D, BS, KB, VB>(piece, a.k_pool, a.v_pool, 0u, 0u, a.kv_heads, kvh, 0) -
                              cpool[i]);
         cstride[i] = (int64_t)a.kv_heads * BS * D * (is_k ? KB : VB);
         cone[i] = __builtin_amdgcn_readfirstlane((is_k ? c / KPT : (c - 2 * KPT) / VPT) == 1 ? 1 : 0);
         cdst[i] = __builtin_amdgcn_readfirstlane((c - lane) * 16);
     }
+    // this lane's piece rotation in the swizzled K and V tile images
+    const int ksw = Swz<D, KB>::PP > 1 ? (((g * 16 + m) * Swz<D, KB>::PP) >> 4) & (Swz<D, KB>::PP - 1) : 0;
+    const int vsw = Swz<D, VB>::PP > 1 ? (((g * D + (D / 16) * m) * 4 * VB / 16) >> 4) & (Swz<D, VB>::PP - 1) : 0;
     auto issue = [&](int st) {
         const int p = st * kStep;
         uint32_t b0, b1;
@@ -402,7 +423,7 @@ void prefill_kernel(PrefillArgs a) {
                 const bf16x8 *kp = reinterpret_cast<const bf16x8 *>(&lds[buf][t * KTILE + (g * 16 + m) * Q4 * 2]);
                 bf16x8 kb[KK];
 #pragma unroll
-                for (int kk = 0; kk < KK; ++kk) kb[kk] = kp[kk];
+                for (int kk = 0; kk < KK; ++kk) kb[kk] = kp[kk ^ ksw];
 #pragma unroll
                 for (int j = 0; j < kNR; ++j) {
                     sc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -415,8 +436,8 @@ void prefill_kernel(PrefillArgs a) {
                 v8i ka[NC];
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    u32x4 k0 = kp[2 * c], k1 = u32x4{0u, 0u, 0u, 0u};
-                    if (NW > 4) k1 = kp[2 * c + 1];
+                    u32x4 k0 = kp[(2 * c) ^ ksw], k1 = u32x4{0u, 0u, 0u, 0u};
+                    if (NW > 4) k1 = kp[(2 * c + 1) ^ ksw];
                     ka[c] = v8i{(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
                                 (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
                 }
@@ -522,7 +543,7 @@ void prefill_kernel(PrefillArgs a) {
                 const u32x4 *vp = reinterpret_cast<const u32x4 *>(
                     &lds[buf][2 * KTILE + t * VTILE + (g * D + (D / 16) * m) * 4 * 2]);
 #pragma unroll
-                for (int i = 0; i < NW / 2; ++i) vv[t][i] = vp[i];
+                for (int i = 0; i < NW / 2; ++i) vv[t][i] = vp[i ^ vsw];
             }
             if (tail) {
 #pragma unroll
@@ -555,7 +576,7 @@ void prefill_kernel(PrefillArgs a) {
                     &lds[buf][2 * KTILE + t * VTILE + (g * D + (D / 16) * m) * 4]);
 #pragma unroll
                 for (int i = 0; i < NW / 4; ++i) {
-                    const u32x4 vq = vp[i];
+                    const u32x4 vq = vp[i ^ vsw];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) vw[t][4 * i + e] = vq[e];
                 }
