@@ -21,8 +21,9 @@
 //     layout (lane (n, g) holds tokens 4g..4g+3 of head n) is exactly the B
 //     operand of the next product;
 //   * O^T[d][head] += V^T P^T on v_mfma_f32_16x16x32_f16 for E4M3 V (codes ->
-//     f16 exact, P in f16), or on the bf16 MFMA for a bf16 V pool with P
-//     split into two bf16 terms, over 32 tokens per instruction;
+//     f16 exact, P split into two f16 terms), or on the bf16 MFMA for a bf16
+//     V pool with P split into two bf16 terms, over 32 tokens per
+//     instruction;
 //   * the online softmax runs in the log2 domain against a per-head reference
 //     max that only moves when a score exceeds it by more than 2^8 (lazy
 //     rescale), with per-lane partial sums.
@@ -167,13 +168,19 @@ struct SoftmaxState {
     float run_sum;
 };
 
+// Smallest positive normal fp32 value.  A split partial may hold an infinity
+// (bf16 V); the reduce never weights it by an underflowed 0 (0 * Inf = NaN):
+// a weight below this is raised to it, which changes a finite result by less
+// than 2^-126 of that partial.
+constexpr float kMinNormal = 0x1p-126f;
+
 // One 32-token step of one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
 // E4M3 K codes become bf16 exactly; bf16 K words are the operand as they are.
-// E4M3 V codes become f16 exactly (P in f16); bf16 V uses the bf16 product
-// with P as a sum of two bf16 terms.
+// E4M3 V codes become f16 exactly, with P as a sum of two f16 terms; bf16 V
+// uses the bf16 product with P as a sum of two bf16 terms.
 template <int D, int KB, int VB>
 __device__ __forceinline__ void compute_step(SoftmaxState<D> &st, StepRegs<D, KB, VB> &cur, const bf16x8 *qb,
-                                             int p, int c1, int g, float qk_scale) {
+                                             int p, int c1, int m, int g, float qk_scale, int *vflags) {
     constexpr int KK = D / 32;
     constexpr int MT = D / 16;
     using R = StepRegs<D, KB, VB>;
@@ -257,19 +264,61 @@ __device__ __forceinline__ void compute_step(SoftmaxState<D> &st, StepRegs<D, KB
 
     // ---- O^T += V^T P^T
     if constexpr (VB == 1) {
-        const f16x8 pb = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3],
-                          (_Float16)pr[4], (_Float16)pr[5], (_Float16)pr[6], (_Float16)pr[7]};
+        // P as two f16 terms, hi = f16(P) and lo = f16(P - hi), about 22
+        // significant bits: one f16 term (11 bits) leaves an error of up to
+        // 2^-12 |V| per output, 2.5e-3 with the outlier channels of the
+        // Llama-shaped workload.  The extra products are free in this
+        // HBM-bound loop.
+        f16x8 ph, pl;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            ph[i] = (_Float16)pr[i];
+            pl[i] = (_Float16)(pr[i] - (float)ph[i]);
+        }
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
             const f16x2 e0 = codes_to_f16x2<false>(cur.vw(0, j)), e1 = codes_to_f16x2<true>(cur.vw(0, j));
             const f16x2 e2 = codes_to_f16x2<false>(cur.vw(1, j)), e3 = codes_to_f16x2<true>(cur.vw(1, j));
             const f16x8 va = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
-            st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, st.acc[j], 0, 0, 0);
+            st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph, st.acc[j], 0, 0, 0);
+            st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pl, st.acc[j], 0, 0, 0);
         }
     } else {
+        // Non-finite bf16 V values.  The definition sums p_t V_t with p_t > 0
+        // for every token of the sequence, so a token holding +-Inf makes that
+        // output dim an infinity of its sign (NaN with both signs) and a NaN
+        // makes it NaN, whatever the token's probability.  In the product a P
+        // term that is 0 (an exactly representable P has lo = 0; a tiny P
+        // underflows) would turn an infinity into NaN instead.  So such values
+        // are taken out of the product (zeroed) and their classes are ORed
+        // into this wave's per-dim flags, which the combine adds back.  Tokens
+        // past the chunk were zeroed above; every other token of the step is
+        // seen by every head.
+        uint32_t nf = 0;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < R::NV; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) nf |= bf16_nonfinite_halves(cur.v[t][i][e]);
+        if (__any(nf != 0u)) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < R::NV; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t w = cur.v[t][i][e];
+                        const uint32_t n = bf16_nonfinite_halves(w);
+                        if (!n) continue;
+                        // word 4i + e holds two tokens of dim (D/16)m + 2i + e/2
+                        atomicOr(&vflags[(D / 16) * m + 2 * i + (e >> 1)], bf16_class_bits(w, n));
+                        cur.v[t][i][e] = w & ~((n >> 15) * 0xFFFFu);
+                    }
+        }
         // P as two bf16 terms, hi = bf16(P) and lo = bf16(P - hi): about 16
-        // significant bits, as precise as the f16 P of the E4M3 path (a single
-        // bf16 P keeps 8).  The extra products are free in this HBM-bound loop.
+        // significant bits, as precise as one f16 term (a single bf16 P keeps
+        // 8).  The extra products are free in this HBM-bound loop.
         bf16x8 ph, pl;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -321,7 +370,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     static_assert(NBUF == 2 || NBUF == 3, "the ring tail below handles up to two remaining steps");
     using Regs = StepRegs<D, KB, VB>;
 
-    extern __shared__ float smem[];   // [waves][G] max, [waves][G] sum, [waves][G][D] acc
+    // [waves][G] max, [waves][G] sum, [waves][G][D] acc; with a bf16 V pool
+    // then [waves][D] flags of the non-finite values taken out of the product
+    extern __shared__ float smem[];
 
     int pair, split;
     if (!decode_unit(blockIdx.x, a, pair, split)) return;   // padding unit
@@ -340,6 +391,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     float *s_max = smem;
     float *s_sum = smem + kWaves * G;
     float *s_acc = smem + 2 * kWaves * G;
+    int *s_flags = reinterpret_cast<int *>(smem + kWaves * G * (2 + D));
+    int *vflags = s_flags + wave * D;
+    if constexpr (VB == 2) {
+        for (int d = lane; d < D; d += 64) vflags[d] = 0;
+    }
 
     if (c0 >= c1) {
         if (a.splits == 1) {      // empty sequence: zero output
@@ -409,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         // keep the next NBUF-1 steps' loads in flight while this one computes
         issue(buf[(u + NBUF - 1) % NBUF], step + NBUF - 1);
         wait_step<LOADS * (NBUF - 1)>(buf[u]);
-        compute_step<D, KB, VB>(st, buf[u], qb, p0 + step * stride, c1, g, a.qk_scale);
+        compute_step<D, KB, VB>(st, buf[u], qb, p0 + step * stride, c1, m, g, a.qk_scale, vflags);
     };
     const int full = nsteps - nsteps % NBUF;
     for (int i = 0; i < full; i += NBUF) {
@@ -463,6 +519,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
             num += f * s_acc[((int64_t)w * G + hn) * D + d];
             den += f * s_sum[w * G + hn];
         }
+        if constexpr (VB == 2) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) c |= (uint32_t)s_flags[w * D + d];
+            num += nonfinite_from_bits(c);
+        }
         const int head = kvh * G + hn;
         if (a.splits == 1) {
             store_out(a.out, ((int64_t)b * a.q_heads + head) * D + d, num * a.v_scale / den, a.out_bf16);
@@ -509,7 +571,9 @@ __global__ __launch_bounds__(D) void decode_reduce(DecodeArgs a) {
         if (t < n) {
             const float *p = part + (int64_t)(i0 + t) * (D + 2);
             const float mi = p[0];
-            s_w[t] = mi == -__builtin_inff() ? 0.0f : exp2f(mi - M);
+            // raised to the smallest normal, so that a partial holding an
+            // infinity (bf16 V) is never multiplied by 0
+            s_w[t] = mi == -__builtin_inff() ? 0.0f : fmaxf(exp2f(mi - M), kMinNormal);
         }
         __syncthreads();
         const float *p = part + (int64_t)i0 * (D + 2);
@@ -539,7 +603,7 @@ __global__ __launch_bounds__(D) void decode_reduce(DecodeArgs a) {
 template <int D, int BS, int KB, int VB>
 hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     const int G = a.q_heads / a.kv_heads;
-    const size_t smem = sizeof(float) * (size_t)kWaves * G * (2 + D);
+    const size_t smem = sizeof(float) * (size_t)kWaves * G * (2 + D) + (VB == 2 ? sizeof(int) * kWaves * D : 0);
     const uint32_t units = (uint32_t)a.splits * (uint32_t)(((a.num_seqs * a.kv_heads + 7) >> 3) << 3);
     hipLaunchKernelGGL((decode_kernel<D, BS, KB, VB>), dim3(units), dim3(kThreads), smem, stream, a);
     hipError_t e = hipGetLastError();

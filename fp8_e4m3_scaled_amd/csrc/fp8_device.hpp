@@ -55,6 +55,41 @@ __device__ __forceinline__ bool has_nan4(uint32_t w) {
     return (((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u) != 0u;
 }
 
+// Bit 7 of every byte of w that holds an E4M3 NaN code (0x7F or 0xFF).
+__device__ __forceinline__ uint32_t e4m3_nan_bytes(uint32_t w) {
+    return ((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+}
+
+// Bit 15 of every 16-bit half of w that holds a bf16 infinity or NaN
+// (exponent field all ones).
+__device__ __forceinline__ uint32_t bf16_nonfinite_halves(uint32_t w) {
+    return ((w & 0x7F807F80u) + 0x00800080u) & 0x80008000u;
+}
+
+// Class bits of the non-finite halves n (bf16_nonfinite_halves) of w: 1 for
+// a NaN, 2 for +Inf, 4 for -Inf.
+__device__ __forceinline__ uint32_t bf16_class_bits(uint32_t w, uint32_t n) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (!((n >> (16 * h + 15)) & 1u)) continue;
+        const uint32_t v = (w >> (16 * h)) & 0xFFFFu;
+        c |= (v & 0x7Fu) ? 1u : (v & 0x8000u) ? 4u : 2u;
+    }
+    return c;
+}
+
+// What non-finite values of the classes c (bf16_class_bits, ORed) add to a sum
+// of products with positive weights: NaN if any is NaN or both infinities
+// occur, else an infinity of the one sign, else 0.
+__device__ __forceinline__ float nonfinite_from_bits(uint32_t c) {
+    if (c & 1u) return __builtin_nanf("");
+    float t = 0.0f;
+    if (c & 2u) t = __builtin_inff();
+    if (c & 4u) t = t - __builtin_inff();          // +Inf - Inf is NaN
+    return t;
+}
+
 // Multiply a bf16 value by the reciprocal scale; a NaN input keeps its own
 // sign (the sign of a NaN produced by an arithmetic operation is not fixed
 // by IEEE 754).

@@ -40,8 +40,13 @@ static_assert(kRows == kPrefillRows, "host launch checks assume this tile height
 constexpr float kLazy = 8.0f;
 constexpr float kNoMax = -1.0e30f;
 constexpr int kUnitScale = 127;          // E8M0 exponent of 1.0 for the scaled fp8 MFMA
+constexpr int kLoScale = 127 - 5;        // E8M0 exponent of 2^-5: Q's lo term is stored times 32
 
-typedef __attribute__((ext_vector_type(8))) int v8i;     // running-max sentinel (finite: see the accumulators)
+typedef __attribute__((ext_vector_type(8))) int v8i;
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+
+template <bool B>
+struct Flag { static constexpr bool value = B; };     // running-max sentinel (finite: see the accumulators)
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -155,10 +160,11 @@ __device__ __forceinline__ const uint8_t *chunk_src(int c, const uint8_t *k_pool
     return v_pool + (base + (int64_t)(tb / 4) * D * 4 + e) * VB;
 }
 
-// Three waves per SIMD for E4M3 pools with head dims up to 128 (a budget of
-// 168 VGPRs); two with a bf16 pool (wider operands, twice the LDS per step).
+// Three waves per SIMD with an E4M3 V pool and head dims up to 128 (a budget
+// of 168 VGPRs; the main loop does not spill, with E4M3 or bf16 K); two with a
+// bf16 V pool (the two-term P and wider operands need more registers).
 template <int D, int KB, int VB>
-struct Occupancy { static constexpr int WAVES = D > 128 ? 1 : (KB == 1 && VB == 1 ? 3 : 2); };
+struct Occupancy { static constexpr int WAVES = D > 128 ? 1 : (VB == 1 ? 3 : 2); };
 
 template <int D, int BS, int KB, int VB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occupancy<D, KB, VB>::WAVES)))
@@ -209,15 +215,22 @@ void prefill_kernel(PrefillArgs a) {
     // g of row n's dims (byte e = dim g*D/4 + e, the K tile's order).
     //
     // S^T = K Q^T runs on the fp8 MFMA with the K codes as they are in the
-    // cache.  Q is split exactly into two E4M3 terms per row: with 2^e the
-    // power of two that puts the row's max |q| in [128, 256),
-    //   y = q * 2^e,  hi = E4M3(y),  lo = E4M3(y - hi),
-    // and hi + lo == y for every element with |y| >= 1/4 (a bf16 significand
+    // cache.  Q is split into two E4M3 terms per row: with 2^e the power of
+    // two that puts the row's max |q| in [128, 256),
+    //   y = q * 2^e,  hi = E4M3(y),  lo = E4M3(32 (y - hi)),
+    // and the lo product runs with the MFMA's block scale 2^-5, so the
+    // score is K.(hi + lo/32).  |y - hi| <= 8 (half a step of E4M3 at
+    // [128, 256)), so 32 (y - hi) <= 256 never saturates; a bf16 significand
     // has 8 bits, E4M3 keeps 4, and the remainder of the round-to-nearest is
-    // a 4-bit multiple of y's last place); smaller elements are off by at
-    // most 2^-10, i.e. 2^-17 of the row max.  So K.(hi + lo) = 2^e (K.q) to
-    // fp32 accumulation, and 2^-e goes into the row's exp2 factor.  A
-    // negative qk_scale flips the sign of y (exact).
+    // a 4-bit multiple of y's last place, so hi + lo/32 == y for every
+    // element with |y| >= 2^-7 (within 2^-15 of the row max); smaller
+    // elements are off by at most 2^-15, i.e. 2^-22 of the row max.  So
+    // K.(hi + lo/32) = 2^e (K.q) to fp32 accumulation, and 2^-e goes into the
+    // row's exp2 factor.  e is capped so that 2^e and the row factor
+    // qk 2^-e stay normal fp32 numbers: a row whose max |q| is below 2^-119
+    // (bf16 subnormals) gets y below 2^7 and scores of no weight, as the
+    // definition's scores are then below 1e-30.  A negative qk_scale flips
+    // the sign of y (exact).
     //
     // With a bf16 K pool the product runs on the bf16 MFMA instead, with Q as
     // given (sign folded in, exact) and no 2^e.
@@ -270,9 +283,10 @@ void prefill_kernel(PrefillArgs a) {
         } else {
             int ex = 0;
             if (!bad && amax > 0.0f) {
-                int E;
+                int E, Eq;
                 (void)frexpf(amax, &E);         // amax = f * 2^E, f in [0.5, 1)
-                ex = 8 - E;
+                (void)frexpf(qk, &Eq);          // qk >= 2^(Eq - 1)
+                ex = min(8 - E, min(126, Eq + 125));
             }
             qk_row[j] = ldexpf(qk, -ex);
             const float mul = ldexpf(qsgn, ex);
@@ -288,7 +302,7 @@ void prefill_kernel(PrefillArgs a) {
                 const f32x2 b23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
                 hv[0] = b01[0]; hv[1] = b01[1]; hv[2] = b23[0]; hv[3] = b23[1];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) rv[e] = v[e] - hv[e];          // exact
+                for (int e = 0; e < 4; ++e) rv[e] = (v[e] - hv[e]) * 32.0f;  // exact, |.| <= 256
                 int l = __builtin_amdgcn_cvt_pk_fp8_f32(rv[0], rv[1], 0, false);
                 l = __builtin_amdgcn_cvt_pk_fp8_f32(rv[2], rv[3], l, true);
                 hw[i] = (uint32_t)h;
@@ -321,14 +335,17 @@ void prefill_kernel(PrefillArgs a) {
     f32x4 rsum[kNR];
     float run_sum[kNR];
     float run_max[kNR];
+    auto reset = [&]() {
 #pragma unroll
-    for (int j = 0; j < kNR; ++j) {
+        for (int j = 0; j < kNR; ++j) {
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        rsum[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        run_sum[j] = 0.0f;
-        run_max[j] = kNoMax;
-    }
+            for (int t = 0; t < MT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            rsum[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            run_sum[j] = 0.0f;
+            run_max[j] = kNoMax;
+        }
+    };
+    reset();
 
     // Block ids come through the constant address space: the index is uniform,
     // so these are scalar loads (lgkmcnt), not vector loads that would make
@@ -393,37 +410,32 @@ void prefill_kernel(PrefillArgs a) {
         }
     };
 
-#pragma unroll
-    for (int i = 0; i < kStages - 1; ++i) issue(i);
-    const int first_row_pos = ctx + i0;
-    for (int s = 0; s < nsteps; ++s) {
-        const int p = s * kStep;
-        const int buf = s % kStages;
-        wait_vmcnt<(kStages - 2) * CH>();   // this wave's share of step s has landed
-        // Everyone's share has, and every wave is done with step s-1's stage.
-        // A bare s_barrier: the workgroup release fence of __syncthreads would
-        // also wait for the transfers still in flight.  The ds_reads of step
-        // s-1 were consumed by its MFMAs, so none is pending here.
-        asm volatile("s_barrier" ::: "memory");
-        __builtin_amdgcn_s_setprio(0);
-        issue(s + kStages - 1);
+    // Careful pass only: per dim of this lane's V operand ((D/16)m + i), the
+    // first key of each non-finite class that was taken out of the product
+    // (0 NaN; for bf16 V also 1 +Inf, 2 -Inf).
+    constexpr int NCLS = VB == 1 ? 1 : 3;
+    int cfirst[NCLS][D / 16];
 
-        const bool diag = p + kStep > first_row_pos;      // some key may be past some row
-        const bool tail = p + kStep > total;              // keys past the sequence's cache
+    // One 32-key step at keys p .. p+31: S^T = K Q^T, causal mask, online
+    // softmax, O^T += V^T P^T.  kpiece(t, i) / vpiece(t, i) return the lane's
+    // i-th 16-byte piece of its K key / V key group in 16-key tile t; diag:
+    // some key may be past some row; tail: some key is past the sequence.
+    // CAREFUL: non-finite V values are taken out of the product (below).
+    auto compute = [&](const int p, const bool diag, const bool tail, auto kpiece, auto vpiece, auto careful_tag) {
+        constexpr bool kCareful = decltype(careful_tag)::value;
         // ---- S^T for both row tiles, one 16-key K tile at a time (its codes
-        // are read from LDS right before its MFMAs, as they are: the lane's
-        // D/4 codes of the key), then the row maxima, then one wave vote for
-        // the lazy rescale: straight-line code for both tiles between the
-        // vote's branches, so their latency chains can interleave.
+        // are read right before its MFMAs, as they are: the lane's D/4 codes
+        // of the key), then the row maxima, then one wave vote for the lazy
+        // rescale: straight-line code for both tiles between the vote's
+        // branches, so their latency chains can interleave.
         f32x4 sc[kNR][2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             if constexpr (KB == 2) {
                 // bf16 K: the lane's D/4 values of key m, quarter g, as KK operands
-                const bf16x8 *kp = reinterpret_cast<const bf16x8 *>(&lds[buf][t * KTILE + (g * 16 + m) * Q4 * 2]);
                 bf16x8 kb[KK];
 #pragma unroll
-                for (int kk = 0; kk < KK; ++kk) kb[kk] = kp[kk ^ ksw];
+                for (int kk = 0; kk < KK; ++kk) kb[kk] = __builtin_bit_cast(bf16x8, kpiece(t, kk));
 #pragma unroll
                 for (int j = 0; j < kNR; ++j) {
                     sc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -432,12 +444,11 @@ void prefill_kernel(PrefillArgs a) {
                         sc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qb[j][kk], sc[j][t], 0, 0, 0);
                 }
             } else {
-                const u32x4 *kp = reinterpret_cast<const u32x4 *>(&lds[buf][t * KTILE + (g * 16 + m) * Q4]);
                 v8i ka[NC];
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    u32x4 k0 = kp[(2 * c) ^ ksw], k1 = u32x4{0u, 0u, 0u, 0u};
-                    if (NW > 4) k1 = kp[(2 * c + 1) ^ ksw];
+                    u32x4 k0 = kpiece(t, 2 * c), k1 = u32x4{0u, 0u, 0u, 0u};
+                    if (NW > 4) k1 = kpiece(t, 2 * c + 1);
                     ka[c] = v8i{(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
                                 (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
                 }
@@ -449,7 +460,7 @@ void prefill_kernel(PrefillArgs a) {
                         sc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[c], qh[j][c], sc[j][t], 0,
                                                                                     0, 0, kUnitScale, 0, kUnitScale);
                         sc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[c], ql[j][c], sc[j][t], 0,
-                                                                                    0, 0, kUnitScale, 0, kUnitScale);
+                                                                                    0, 0, kUnitScale, 0, kLoScale);
                     }
                 }
             }
@@ -531,7 +542,7 @@ void prefill_kernel(PrefillArgs a) {
         // that the SIMD's other waves fill the matrix cores' shadow with their
         // softmax work rather than the other way round (~2.5 %); the priority
         // drops back after the next step's barrier.
-        __builtin_amdgcn_s_setprio(1);
+        if constexpr (!kCareful) __builtin_amdgcn_s_setprio(1);
         // ---- O^T += V^T P^T, V operands read now and converted once for
         // both row tiles (lane (m, g) holds keys 4g..4g+3 of dims (D/16)m..)
         if constexpr (VB == 2) {
@@ -539,12 +550,9 @@ void prefill_kernel(PrefillArgs a) {
             // two dims, split into the operands of output tiles 2i and 2i+1
             u32x4 vv[2][NW / 2];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const u32x4 *vp = reinterpret_cast<const u32x4 *>(
-                    &lds[buf][2 * KTILE + t * VTILE + (g * D + (D / 16) * m) * 4 * 2]);
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int i = 0; i < NW / 2; ++i) vv[t][i] = vp[i ^ vsw];
-            }
+                for (int i = 0; i < NW / 2; ++i) vv[t][i] = vpiece(t, i);
             if (tail) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
@@ -555,6 +563,29 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                     for (int i = 0; i < NW / 2; ++i) vv[t][i] &= keep;
                 }
+            }
+            if constexpr (kCareful) {
+                // word e of piece i holds keys 2(e % 2), +1 of the lane's group
+                // for dim (D/16)m + 2i + e/2
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < NW / 2; ++i)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t w = vv[t][i][e];
+                            const uint32_t n = bf16_nonfinite_halves(w);
+                            if (!n) continue;
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) {
+                                if (!((n >> (16 * h + 15)) & 1u)) continue;
+                                const uint32_t v = (w >> (16 * h)) & 0xFFFFu;
+                                const int key = p + 16 * t + 4 * g + 2 * (e & 1) + h;
+                                int &f = cfirst[(v & 0x7Fu) ? 0 : (v & 0x8000u) ? 2 : 1][2 * i + (e >> 1)];
+                                f = min(f, key);
+                            }
+                            vv[t][i][e] = w & ~((n >> 15) * 0xFFFFu);
+                        }
             }
 #pragma unroll
             for (int i = 0; i < NW / 2; ++i) {
@@ -572,11 +603,9 @@ void prefill_kernel(PrefillArgs a) {
             uint32_t vw[2][NW];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const u32x4 *vp = reinterpret_cast<const u32x4 *>(
-                    &lds[buf][2 * KTILE + t * VTILE + (g * D + (D / 16) * m) * 4]);
 #pragma unroll
                 for (int i = 0; i < NW / 4; ++i) {
-                    const u32x4 vq = vp[i ^ vsw];
+                    const u32x4 vq = vpiece(t, i);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) vw[t][4 * i + e] = vq[e];
                 }
@@ -589,6 +618,19 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                     for (int i = 0; i < NW; ++i) vw[t][i] &= keep;
                 }
+            }
+            if constexpr (kCareful) {
+                // word i holds keys 4g..4g+3 (bytes 0..3) of dim (D/16)m + i;
+                // the lowest NaN byte is the word's first NaN key
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < NW; ++i) {
+                        const uint32_t n = e4m3_nan_bytes(vw[t][i]);
+                        if (!n) continue;
+                        cfirst[0][i] = min(cfirst[0][i], p + 16 * t + 4 * g + (int)(__builtin_ctz(n) >> 3));
+                        vw[t][i] &= ~((n >> 7) * 0xFFu);
+                    }
             }
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
@@ -605,9 +647,116 @@ void prefill_kernel(PrefillArgs a) {
             for (int j = 0; j < kNR; ++j)
                 rsum[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[j], rsum[j], 0, 0, 0);
         }
-    }
+    };
+
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i) issue(i);
+    const int first_row_pos = ctx + i0;
+    // One step of the main pass: operands from the step's LDS image.  Steps
+    // before the first one that reaches the tile's first query position need
+    // no causal mask (DIAG false); every step from there on, the sequence's
+    // tail included, runs the DIAG form.  Two loops keep the diagonal steps'
+    // extra values out of the main loop's registers.
+    auto step = [&](const int s, auto diag_tag) {
+        constexpr bool kDiag = decltype(diag_tag)::value;
+        const int p = s * kStep;
+        const int buf = s % kStages;
+        wait_vmcnt<(kStages - 2) * CH>();   // this wave's share of step s has landed
+        // Everyone's share has, and every wave is done with step s-1's stage.
+        // A bare s_barrier: the workgroup release fence of __syncthreads would
+        // also wait for the transfers still in flight.  The ds_reads of step
+        // s-1 were consumed by its MFMAs, so none is pending here.
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_s_setprio(0);
+        issue(s + kStages - 1);
+        const u32x4 *kimg = reinterpret_cast<const u32x4 *>(&lds[buf][(g * 16 + m) * Q4 * KB]);
+        const u32x4 *vimg = reinterpret_cast<const u32x4 *>(&lds[buf][2 * KTILE + (g * D + (D / 16) * m) * 4 * VB]);
+        compute(p, kDiag, kDiag && p + kStep > total,
+                [&](int t, int i) { return kimg[t * (KTILE / 16) + (i ^ ksw)]; },
+                [&](int t, int i) { return vimg[t * (VTILE / 16) + (i ^ vsw)]; }, Flag<false>{});
+    };
+    const int s_diag = min(nsteps, first_row_pos / kStep);
+    for (int s = 0; s < s_diag; ++s) step(s, Flag<false>{});
+    for (int s = s_diag; s < nsteps; ++s) step(s, Flag<true>{});
     __builtin_amdgcn_s_setprio(0);
     wait_vmcnt<0>();    // no LDS write may still be in flight when the workgroup ends
+
+    // ---- Non-finite V values.  The definition sums over the keys a row sees
+    // and only those, so a NaN V (a storable E4M3 code; bf16 pools keep NaN
+    // and infinities) at a key past a row must not reach that row, and a seen
+    // +-Inf makes the dim an infinity of its sign (NaN with both signs)
+    // whatever the key's probability.  In the main pass such a value meets a
+    // zero probability (a key past the row, an underflowed or exactly
+    // representable P with lo = 0) as 0 * NaN or 0 * Inf, and a probability
+    // P > 0 as NaN or +-Inf: either way an accumulator ends non-finite, and
+    // it stays so (a rescale by a positive factor keeps it).  So a wave whose
+    // accumulators are all finite saw none, and one that has a non-finite
+    // accumulator runs its rows again in a careful pass: operands straight
+    // from the cache in HBM (no LDS, no barrier; the other waves are done with
+    // the stages), non-finite V values taken out of the product, and for each
+    // dim the first key of each class; a row sees a prefix of the keys, so
+    // afterwards the (dim, row) gets NaN when the row sees a NaN or both
+    // infinities, else an infinity of the sign it sees.  (A NaN score, from a
+    // NaN K code or q, makes its rows NaN in both passes.)
+    float amax_acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kNR; ++j)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) amax_acc = vmax(amax_acc, fabsf(acc[j][t][i]));
+    if (__any(!(amax_acc < __builtin_inff()))) {
+        reset();
+#pragma unroll
+        for (int c = 0; c < NCLS; ++c)
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i) cfirst[c][i] = 0x7FFFFFFF;
+        for (int s = 0; s < nsteps; ++s) {
+            const int p = s * kStep;
+            uint32_t b0, b1;
+            blocks_of(p, b0, b1);
+            const uint8_t *kt[2], *vt[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int64_t base = ((int64_t)(t ? b1 : b0) * a.kv_heads + kvh) * (BS * D);   // elements
+                const int tb = (p + 16 * t) % BS;
+                kt[t] = a.k_pool + (base + (int64_t)(g * BS + tb + m) * Q4) * KB;
+                vt[t] = a.v_pool + (base + (int64_t)((tb / 4 + g) * D + (D / 16) * m) * 4) * VB;
+            }
+            compute(p, p + kStep > first_row_pos, p + kStep > total,
+                    [&](int t, int i) { return reinterpret_cast<const u32x4 *>(kt[t])[i]; },
+                    [&](int t, int i) { return reinterpret_cast<const u32x4 *>(vt[t])[i]; }, Flag<true>{});
+        }
+        // first keys over the row's four k-groups, then into the lanes that
+        // hold the dims: acc[j][t][i] of lane (n, g) is dim (D/16)(4g + i) + t,
+        // whose V operand lane is 4g + i
+#pragma unroll
+        for (int c = 0; c < NCLS; ++c)
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t) {
+                int f = cfirst[c][t];
+                f = min(f, __shfl_xor(f, 16));
+                cfirst[c][t] = min(f, __shfl_xor(f, 32));
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                int f[NCLS];
+#pragma unroll
+                for (int c = 0; c < NCLS; ++c) f[c] = __shfl(cfirst[c][t], 4 * g + i);
+#pragma unroll
+                for (int j = 0; j < kNR; ++j) {
+                    float term = 0.0f;
+                    if constexpr (NCLS > 1) {
+                        if (f[1] <= row_pos[j]) term = __builtin_inff();
+                        if (f[2] <= row_pos[j]) term = term - __builtin_inff();   // +Inf - Inf is NaN
+                    }
+                    if (f[0] <= row_pos[j]) term = __builtin_nanf("");
+                    acc[j][t][i] += term;
+                }
+            }
+    }
 
     // ---- normalize and write: lane (n, g) holds rows n of its tiles, dims (D/16)(4g+r)+t
 #pragma unroll

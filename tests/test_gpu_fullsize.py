@@ -26,7 +26,7 @@ import fp8_e4m3_scaled_amd as kv
 import oracle
 from synth import Workload, bf16_bits
 from tests.gpu_util import DEV, log, t_dev
-from tests.test_gpu_decode import assert_close
+from tests.test_gpu_decode import ATOL, assert_close
 
 pytestmark = pytest.mark.gpu
 
@@ -126,17 +126,30 @@ class OraclePools:
         return np.stack(_pmap(one, range(w.B)))
 
 
-def _decode_full(w, cache, q, lens):
-    """One decode launch over the whole batch, bf16 out, as the benchmark runs it."""
+def _decode_full(w, cache, q, lens, tables=None):
+    """One decode launch over the whole batch, as the benchmark runs it, once
+    with bf16 outputs and once with fp32 outputs: {dtype: [B][Hq][D]}."""
     max_len = int(lens.max())
     ws_bytes = kv.paged_attn_decode_workspace(cache.handle, w.B, w.Hq, max_len)
     ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=DEV)
-    out = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.bfloat16, device=DEV)
-    kv.paged_attn_decode(cache.handle, 0, q, w.Hq, t_dev(w.block_tables.astype(np.int32)), w.max_blocks,
-                         t_dev(lens.astype(np.int32)), w.B, max_len, w.sm_scale(), out, kv.DTYPE_BF16,
-                         ws, ws_bytes)
-    torch.cuda.synchronize()
-    return out.float().cpu().numpy(), ws_bytes
+    tables = t_dev(w.block_tables.astype(np.int32)) if tables is None else tables
+    got = {}
+    for dt, tdt in ((kv.DTYPE_BF16, torch.bfloat16), (kv.DTYPE_F32, torch.float32)):
+        out = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=tdt, device=DEV)
+        kv.paged_attn_decode(cache.handle, 0, q, w.Hq, tables, w.max_blocks, t_dev(lens.astype(np.int32)), w.B,
+                             max_len, w.sm_scale(), out, dt, ws, ws_bytes)
+        torch.cuda.synchronize()
+        got[dt] = out.float().cpu().numpy()
+    return got, ws_bytes
+
+
+def assert_both(got, want, what):
+    """Both output dtypes within |d| <= 2e-3 + 1e-2 |ref|; fp32 outputs also max |d| <= 2e-3."""
+    assert_close(got[kv.DTYPE_BF16], want, what + " (bf16 out)")
+    assert_close(got[kv.DTYPE_F32], want, what + " (fp32 out)")
+    err = float(np.max(np.abs(got[kv.DTYPE_F32] - want)))
+    log(f"{what}: fp32-output max |d| = {err:.3g}")
+    assert err <= ATOL, f"{what}: fp32-output max |d| {err:.3g} > {ATOL}"
 
 
 @pytest.mark.parametrize("elems", [(kv.ELEM_E4M3, kv.ELEM_E4M3), (kv.ELEM_BF16, kv.ELEM_BF16)],
@@ -170,7 +183,7 @@ def test_llama8b_full_size(elems):
         orc.store([(b, 0, int(w.total_lengths[b])) for b in range(w.B)])
         orc.check_bytes(cache, "llama8b")
         want = orc.decode_all(bf16_bits(q), w.total_lengths)
-        assert_close(got, want, "llama8b decode, every head")
+        assert_both(got, want, "llama8b decode, every head")
     finally:
         cache.close()
 
@@ -196,7 +209,7 @@ def test_varlen_full_size():
         orc.store([(b, 0, int(w.total_lengths[b])) for b in range(w.B)])
         orc.check_bytes(cache, "varlen")
         want = orc.decode_all(bf16_bits(q), w.total_lengths)
-        assert_close(got, want, "varlen decode, every head")
+        assert_both(got, want, "varlen decode, every head")
     finally:
         cache.close()
 
@@ -222,13 +235,13 @@ def test_longctx_full_size_with_shift():
         got2, _ = _decode_full(w, cache, q, lens)
         orc = OraclePools(w, cache.ks, cache.vs)
         orc.store([(b, 0, int(lens[b])) for b in range(w.B)])
-        assert_close(got1, orc.decode_all(qb, lens), "longctx decode before shift, every head")
+        assert_both(got1, orc.decode_all(qb, lens), "longctx decode before shift, every head")
         # the oracle's own shift, per sequence (disjoint slots)
         _pmap(lambda b: oracle.kshift(orc.kp, w.slots(b, 0, int(lens[b])), Hkv=w.Hkv, D=w.D, BS=w.BS,
                                       delta=w.spec.delta, theta=w.spec.theta, rot_dim=w.D, neox=True),
               range(w.B))
         orc.check_bytes(cache, "longctx after shift")
-        assert_close(got2, orc.decode_all(qb, lens), "longctx decode after shift, every head")
+        assert_both(got2, orc.decode_all(qb, lens), "longctx decode after shift, every head")
     finally:
         cache.close()
 
@@ -253,13 +266,16 @@ def test_prefill_full_size():
         kv.kv_store_fp8(cache.handle, 0, K, V, row, row, sd, T)
         q = w.q_chunk(DEV)
         cu = (np.arange(w.B + 1) * n).astype(np.int32)
-        out = torch.full((T, w.Hq, w.D), float("nan"), dtype=torch.bfloat16, device=DEV)
-        kv.paged_attn_prefill_chunk(cache.handle, 0, q, w.Hq, t_dev(cu), t_dev(ctx),
-                                    t_dev(w.block_tables.astype(np.int32)), w.max_blocks, w.B, T, n,
-                                    int(ctx.max()), w.sm_scale(), out, kv.DTYPE_BF16)
-        torch.cuda.synchronize()
-        got = out.float().cpu().numpy()
-        assert np.isfinite(got).all()
+        got = {}
+        for dt, tdt in ((kv.DTYPE_BF16, torch.bfloat16), (kv.DTYPE_F32, torch.float32)):
+            out = torch.full((T, w.Hq, w.D), float("nan"), dtype=tdt, device=DEV)
+            kv.paged_attn_prefill_chunk(cache.handle, 0, q, w.Hq, t_dev(cu), t_dev(ctx),
+                                        t_dev(w.block_tables.astype(np.int32)), w.max_blocks, w.B, T, n,
+                                        int(ctx.max()), w.sm_scale(), out, dt)
+            torch.cuda.synchronize()
+            got[dt] = out.float().cpu().numpy()
+            assert np.isfinite(got[dt]).all()
+            del out
         orc = OraclePools(w, cache.ks, cache.vs)
         orc.store([(b, 0, int(w.total_lengths[b])) for b in range(w.B)])
         orc.check_bytes(cache, "prefill")
@@ -282,8 +298,15 @@ def test_prefill_full_size():
                                       D=w.D, BS=w.BS, k_scale=cache.ks, v_scale=cache.vs,
                                       sm_scale=w.sm_scale(), sel=sel)
             return sel, ref[sel[:, 0], sel[:, 1]]
+        err = 0.0
         for sel, ref in _pmap(one, sorted(groups)):
-            assert_close(got[sel[:, 0], sel[:, 1]], ref, f"prefill rows of group ({sel[0, 0] // n}, ...)")
+            what = f"prefill rows of group ({sel[0, 0] // n}, ...)"
+            assert_close(got[kv.DTYPE_BF16][sel[:, 0], sel[:, 1]], ref, what + " (bf16 out)")
+            gf = got[kv.DTYPE_F32][sel[:, 0], sel[:, 1]]
+            assert_close(gf, ref, what + " (fp32 out)")
+            err = max(err, float(np.max(np.abs(gf - ref))))
+        log(f"prefill sampled rows: fp32-output max |d| = {err:.3g}")
+        assert err <= ATOL, f"prefill: fp32-output max |d| {err:.3g} > {ATOL}"
         assert len(rows) >= 4096
     finally:
         cache.close()
