@@ -44,6 +44,7 @@ SIGNATURES = {
     "kv_store_fp8": (I32, [P, I32, P, P, I64, I64, P, I64, P]),
     "paged_attn_decode_workspace": (SZ, [P, I32, I32, I32]),
     "paged_attn_decode": (I32, [P, I32, P, I32, P, I32, P, I32, I32, F32, P, I32, P, SZ, P]),
+    "paged_attn_decode_noalloc": (I32, [P, I32, P, I32, P, I32, P, I32, I32, F32, P, I32, P]),
     "paged_attn_prefill_chunk": (I32, [P, I32, P, I32, P, P, P, I32, I32, I64, I32, I32, F32, P,
                                        I32, P]),
     "kv_shift_rope": (I32, [P, I32, P, I64, I32, F32, I32, I32, P]),
@@ -230,6 +231,14 @@ def paged_attn_decode(cache, layer: int, q_bf16, num_q_heads: int, block_tables,
                                   max_blocks_per_seq, _ptr(seq_lens), num_seqs, max_seq_len,
                                   sm_scale, _ptr(out), out_dtype, _ptr(workspace), workspace_bytes,
                                   _stream(stream)))
+
+
+def paged_attn_decode_noalloc(cache, layer: int, q_bf16, num_q_heads: int, block_tables,
+                              max_blocks_per_seq: int, seq_lens, num_seqs: int, max_seq_len: int,
+                              sm_scale: float, out, out_dtype: int, stream=None) -> None:
+    _check(_lib.paged_attn_decode_noalloc(cache, layer, _ptr(q_bf16), num_q_heads, _ptr(block_tables),
+                                          max_blocks_per_seq, _ptr(seq_lens), num_seqs, max_seq_len,
+                                          sm_scale, _ptr(out), out_dtype, _stream(stream)))
 
 
 def paged_attn_prefill_chunk(cache, layer: int, q_bf16, num_q_heads: int, cu_q_lens,

@@ -243,6 +243,11 @@ kvf8_status kv_cache_alloc_typed(int32_t num_layers, int64_t num_blocks, int32_t
         return hip_fail(e, "allocating and clearing the pools");
     }
     c->owned = true;
+    {   // set up the no-allocation decode's scratch on this device now (its
+        // first call would otherwise); a failure here is reported by that call
+        void *ws = nullptr;
+        (void)kvf8::noalloc_scratch(c->device, &ws);
+    }
     *out = c;
     return ok();
 }
@@ -448,12 +453,12 @@ size_t paged_attn_decode_workspace(const kvf8_cache *c, int32_t num_seqs, int32_
     return (size_t)num_seqs * (size_t)num_q_heads * (size_t)splits * (size_t)(c->head_dim + 2) * sizeof(float);
 }
 
-kvf8_status paged_attn_decode(kvf8_cache *c, int32_t layer, const uint16_t *q_bf16,
-                              int32_t num_q_heads, const int32_t *block_tables,
-                              int32_t max_blocks_per_seq, const int32_t *seq_lens,
-                              int32_t num_seqs, int32_t max_seq_len, float sm_scale, void *out,
-                              kvf8_dtype out_dtype, void *workspace, size_t workspace_bytes,
-                              void *stream) {
+namespace {
+
+kvf8_status decode_call(kvf8_cache *c, int32_t layer, const uint16_t *q_bf16, int32_t num_q_heads,
+                        const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                        int32_t num_seqs, int32_t max_seq_len, float sm_scale, void *out, kvf8_dtype out_dtype,
+                        void *workspace, size_t workspace_bytes, void *stream) {
     kvf8_status st = check_layer(c, layer);
     if (st != KVF8_OK) return st;
     if (num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq < 0)
@@ -523,6 +528,44 @@ kvf8_status paged_attn_decode(kvf8_cache *c, int32_t layer, const uint16_t *q_bf
     hipError_t e = kvf8::launch_decode(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "paged_attn_decode launch");
     return ok();
+}
+
+}  // namespace
+
+kvf8_status paged_attn_decode(kvf8_cache *c, int32_t layer, const uint16_t *q_bf16,
+                              int32_t num_q_heads, const int32_t *block_tables,
+                              int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                              int32_t num_seqs, int32_t max_seq_len, float sm_scale, void *out,
+                              kvf8_dtype out_dtype, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+    return decode_call(c, layer, q_bf16, num_q_heads, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                       max_seq_len, sm_scale, out, out_dtype, workspace, workspace_bytes, stream);
+}
+
+kvf8_status paged_attn_decode_noalloc(kvf8_cache *c, int32_t layer, const uint16_t *q_bf16,
+                                      int32_t num_q_heads, const int32_t *block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                                      int32_t num_seqs, int32_t max_seq_len, float sm_scale, void *out,
+                                      kvf8_dtype out_dtype, void *stream) {
+    kvf8_status st = check_layer(c, layer);
+    if (st != KVF8_OK) return st;
+    // 0 for shapes that need no workspace and for invalid arguments, which
+    // decode_call then rejects with their own message
+    const size_t need = paged_attn_decode_workspace(c, num_seqs, num_q_heads, max_seq_len);
+    if (need > kvf8::kNoAllocScratchBytes)
+        return fail(KVF8_E_UNSUPPORTED,
+                    "this decode needs %zu bytes of split-K workspace; paged_attn_decode_noalloc holds %zu "
+                    "(use paged_attn_decode with a workspace)",
+                    need, kvf8::kNoAllocScratchBytes);
+    void *ws = nullptr;
+    if (need > 0) {
+        int dev = 0;
+        hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) : hipGetDevice(&dev);
+        if (e == hipSuccess) e = kvf8::noalloc_scratch(dev, &ws);
+        if (e != hipSuccess) return hip_fail(e, "device scratch of paged_attn_decode_noalloc");
+    }
+    return decode_call(c, layer, q_bf16, num_q_heads, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                       max_seq_len, sm_scale, out, out_dtype, ws, need, stream);
 }
 
 kvf8_status paged_attn_prefill_chunk(kvf8_cache *c, int32_t layer, const uint16_t *q_bf16,

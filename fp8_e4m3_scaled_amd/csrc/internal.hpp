@@ -55,6 +55,14 @@ struct StoreArgs {
 };
 hipError_t launch_store(const StoreArgs &a, hipStream_t stream);
 
+// ---------------------------------------------------------------- no-allocation decode
+// Bytes of the fixed device array that holds paged_attn_decode_noalloc's
+// split-K partials (one per device, for the life of the process).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+// Device address of that array on `device`; looked up on the first call for
+// each device (with that device current), then kept.
+hipError_t noalloc_scratch(int device, void **ptr);
+
 // ---------------------------------------------------------------- prefill constants
 constexpr int kPrefillThreads = 256;  // threads per prefill workgroup (4 waves)
 constexpr int kPrefillRows = 128;     // (query token, head) rows per prefill workgroup

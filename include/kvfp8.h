@@ -271,6 +271,29 @@ kvf8_status paged_attn_decode(kvf8_cache *cache, int32_t layer, const uint16_t *
                               void *stream);
 
 /*
+ * paged_attn_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments and results, without the
+ * workspace arguments.  The split-K partials go into a fixed device array of
+ * 64 MiB that the library holds on each GPU it runs on until the process
+ * ends; its device address is looked up once per device (at kv_cache_alloc
+ * with library-owned pools, else on the first call on that device) and the
+ * call itself allocates nothing.
+ *   - A shape whose workspace (paged_attn_decode_workspace) exceeds 64 MiB
+ *     -> KVF8_E_UNSUPPORTED, before anything is launched.
+ *   - Every call on one GPU uses that GPU's array, which keeps the last
+ *     call's contents (nothing in it needs to start at zero): calls that
+ *     overlap on one GPU (concurrent streams, threads) race and give
+ *     undefined results; calls ordered on one stream do not.
+ *   - The device is the stream's (the current device for a NULL stream).
+ */
+kvf8_status paged_attn_decode_noalloc(kvf8_cache *cache, int32_t layer, const uint16_t *q_bf16,
+                                      int32_t num_q_heads, const int32_t *block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                                      int32_t num_seqs, int32_t max_seq_len, float sm_scale,
+                                      void *out, kvf8_dtype out_dtype, void *stream);
+
+/*
  * Causal attention of a chunk of new query tokens over one layer's cache
  * (chunked prefill).  Sequence b has context_lens[b] tokens cached before
  * its chunk of cu_q_lens[b+1] - cu_q_lens[b] query tokens; query token i of
