@@ -203,10 +203,10 @@ def run_llama8b(args):
         "wall_s_timed": round(wall, 3),
     }
 
-    result["stream_read_ceiling"] = _stream_ceiling(kv, stream)
+    result["stream_read_ceiling"] = _stream_ceiling(stream)
     result["decode"]["frac_of_stream_ceiling"] = round(decode_gbps / result["stream_read_ceiling"]["GBps"], 4)
-    result["paged_gather_ceiling"] = _gather_ceiling(args, kv, handles, tables, w.max_blocks, lens, w.B, w.Hkv,
-                                                     kv_bytes, stream)
+    result["paged_gather_ceiling"] = _gather_ceiling(args, kv, w, handles, tables, w.max_blocks, lens, w.B,
+                                                     w.Hkv, kv_bytes, stream)
     result["decode"]["frac_of_gather_ceiling"] = round(
         decode_gbps / result["paged_gather_ceiling"]["GBps"], 4)
     result["calibrate"] = _calibrate(args, kv, K, V, T, row, ks, vs, stream)
@@ -292,35 +292,39 @@ def _typed_exchange(args, kv, w, K, V, slots_d, T, q, tables, lens, max_len, out
     return res
 
 
-def _gather_ceiling(args, kv, handles, tables, max_blocks, lens, B, Hkv, kv_bytes, stream):
-    """kvf8_gather_probe over the decode's own pools and block tables: a plain
+def _gather_ceiling(args, kv, w, handles, tables, max_blocks, lens, B, Hkv, kv_bytes, stream):
+    """The gather probe over the decode's own pools and block tables: a plain
     read of exactly the K/V tiles the decode reads, the ceiling of its
     scattered-tile access pattern.  GB/s counts the K/V bytes only."""
     import torch
+    import probe
     out = torch.empty(B * Hkv, dtype=torch.int32, device="cuda")
+    pools = [kv.kv_cache_pools(h, 0) for h in handles]
     copies = len(handles)
 
     def call(i):
-        kv.kvf8_gather_probe(handles[(i + 1) % copies], 0, tables, max_blocks, lens, B, out, stream)
+        kp, vp, _ = pools[(i + 1) % copies]
+        probe.gather(kp, vp, w.NB, w.Hkv, w.BS, w.D, 1, 1, tables, max_blocks, lens, B, out, stream)
 
     ms = _timed(call, args.steps, args.warmup, stream).mean()
     gbps = kv_bytes / (ms * 1e-3) / 1e9
     return {"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "ms_mean": round(ms, 5),
-            "bytes": kv_bytes, "kernel": "kvf8_gather_probe (one workgroup per (sequence, kv-head))"}
+            "bytes": kv_bytes, "kernel": "gather_probe (one workgroup per (sequence, kv-head))"}
 
 
-def _stream_ceiling(kv, stream, nbytes=2 << 30, launches=20):
-    """A plain streaming read (kvf8_read_probe) of two alternating 2 GiB buffers:
+def _stream_ceiling(stream, nbytes=2 << 30, launches=20):
+    """A plain streaming read (the read probe) of two alternating 2 GiB buffers:
     the achievable read bandwidth of this part, reported beside the 8 TB/s figure."""
     import torch
+    import probe
     bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
     n_out = 1024
     sink = torch.empty(n_out, dtype=torch.int32, device="cuda")
-    ms = _timed(lambda i: kv.kvf8_read_probe(bufs[i % 2], nbytes, sink, n_out, stream), launches, 3, stream).mean()
+    ms = _timed(lambda i: probe.read(bufs[i % 2], nbytes, sink, n_out, stream), launches, 3, stream).mean()
     gbps = nbytes / (ms * 1e-3) / 1e9
     del bufs
     return {"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes": nbytes,
-            "launches": launches, "kernel": "kvf8_read_probe (XOR-reduce read, 1024 workgroups)"}
+            "launches": launches, "kernel": "read_probe (XOR-reduce read, 1024 workgroups)"}
 
 
 def _host_threads():
@@ -758,9 +762,9 @@ def run_varlen(args):
     # workgroup per (sequence, kv-head) and no split, which the decode's split
     # plan beats on this length mix (long sequences would serialize).
     kv_bytes = int(lens.astype(np.int64).sum()) * 2 * w.Hkv * w.D
-    res["stream_read_ceiling"] = _stream_ceiling(kv, stream)
+    res["stream_read_ceiling"] = _stream_ceiling(stream)
     res["decode"]["frac_of_stream_ceiling"] = round(de_gbps / res["stream_read_ceiling"]["GBps"], 4)
-    res["paged_gather_unsplit"] = _gather_ceiling(args, kv, [h], tables, w.max_blocks, lens_d, w.B, w.Hkv,
+    res["paged_gather_unsplit"] = _gather_ceiling(args, kv, w, [h], tables, w.max_blocks, lens_d, w.B, w.Hkv,
                                                   kv_bytes, stream)
     res["decode"]["speedup_over_unsplit_gather"] = round(de_gbps / res["paged_gather_unsplit"]["GBps"], 4)
     kv.kv_cache_free(h)

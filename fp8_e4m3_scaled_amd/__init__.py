@@ -51,8 +51,6 @@ SIGNATURES = {
     "kv_rope_table": (I32, [P, I32, F32, I32, P]),
     "kv_shift_rope_per_slot": (I32, [P, I32, P, P, I64, P, I32, I32, I32, P]),
     "kv_calibrate_scales": (I32, [P, P, I64, I64, I64, I64, P, P, I32, P]),
-    "kvf8_gather_probe": (I32, [P, I32, P, I32, P, I32, P, P]),
-    "kvf8_read_probe": (I32, [P, SZ, P, I32, P]),
 }
 
 
@@ -279,12 +277,3 @@ def kv_calibrate_scales(k_bf16, v_bf16, k_tok_stride: int, v_tok_stride: int, nu
     _check(_lib.kv_calibrate_scales(_ptr(k_bf16), _ptr(v_bf16), k_tok_stride, v_tok_stride, num_tokens,
                                     row_elems, _ptr(amax), _ptr(scales_out), scale_dtype, _stream(stream)))
 
-
-def kvf8_gather_probe(cache, layer: int, block_tables, max_blocks: int, seq_lens, num_seqs: int, out_words,
-                      stream=None) -> None:
-    _check(_lib.kvf8_gather_probe(cache, layer, _ptr(block_tables), max_blocks, _ptr(seq_lens), num_seqs,
-                                  _ptr(out_words), _stream(stream)))
-
-
-def kvf8_read_probe(buf, nbytes: int, out_words, n_out: int, stream=None) -> None:
-    _check(_lib.kvf8_read_probe(_ptr(buf), nbytes, _ptr(out_words), n_out, _stream(stream)))

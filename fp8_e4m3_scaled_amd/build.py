@@ -24,7 +24,7 @@ ARCH = "gfx950"
 CFLAGS = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-    "-Wall", "-Wextra", "-Wno-unused-parameter",
+    "-Wall", "-Wextra", "-Werror", "-Wno-unused-parameter",
     # packed FP32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # matrix-core accumulators stay in ordinary VGPRs: the softmax rescales them

@@ -790,49 +790,4 @@ kvf8_status kv_calibrate_scales(const uint16_t *k_bf16, const uint16_t *v_bf16, 
     return ok();
 }
 
-kvf8_status kvf8_gather_probe(const kvf8_cache *c, int32_t layer, const int32_t *block_tables,
-                              int32_t max_blocks, const int32_t *seq_lens, int32_t num_seqs, uint32_t *out_words,
-                              void *stream) {
-    kvf8_status st = check_layer(c, layer);
-    if (st != KVF8_OK) return st;
-    if (num_seqs < 0 || max_blocks < 0) return fail(KVF8_E_INVALID, "num_seqs and max_blocks must be >= 0");
-    if (num_seqs == 0) return ok();
-    if (!block_tables || !seq_lens || !out_words)
-        return fail(KVF8_E_INVALID, "block_tables, seq_lens and out_words must be non-NULL");
-    if ((int64_t)num_seqs * c->kv_heads > 0x7FFFFFFF) return fail(KVF8_E_INVALID, "too many (sequence, kv-head) units");
-    auto words_log2 = [&](int eb) {
-        int64_t words = (int64_t)c->block_size * c->head_dim * eb / 16;
-        int l = 0;
-        while ((int64_t(1) << l) < words) ++l;
-        return l;
-    };
-    kvf8::GatherProbeArgs a{};
-    a.k_pool = k_pool_of(c, layer);
-    a.v_pool = v_pool_of(c, layer);
-    a.block_tables = block_tables;
-    a.seq_lens = seq_lens;
-    a.out = out_words;
-    a.num_blocks = c->num_blocks;
-    a.max_blocks = max_blocks;
-    a.num_seqs = num_seqs;
-    a.kv_heads = c->kv_heads;
-    a.block_size = c->block_size;
-    a.k_words_log2 = words_log2(c->k_eb);
-    a.v_words_log2 = words_log2(c->v_eb);
-    hipError_t e = kvf8::launch_gather_probe(a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "kvf8_gather_probe launch");
-    return ok();
-}
-
-kvf8_status kvf8_read_probe(const void *buf, size_t bytes, uint32_t *out_words, int32_t n_out, void *stream) {
-    if (bytes == 0) return ok();
-    if (!buf || !out_words) return fail(KVF8_E_INVALID, "buf and out_words must be non-NULL");
-    if ((reinterpret_cast<uintptr_t>(buf) % 16) != 0 || bytes % 16 != 0)
-        return fail(KVF8_E_INVALID, "buf must be 16-byte aligned and bytes a multiple of 16");
-    if (n_out < 1 || n_out > (1 << 20)) return fail(KVF8_E_INVALID, "n_out must be in [1, 2^20]");
-    hipError_t e = kvf8::launch_read_probe(buf, (int64_t)bytes, out_words, n_out, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "kvf8_read_probe launch");
-    return ok();
-}
-
 }  // extern "C"

@@ -114,7 +114,6 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
-// ---------------------------------------------------------------- read probe
 // ---------------------------------------------------------------- calibration
 struct CalibArgs {
     const uint16_t *x[2];    // K, V bf16 rows (a side may be null when not launched)
@@ -129,8 +128,6 @@ constexpr int64_t kCalibWorkgroups = 2048;   // amax workgroups per launch, over
 // non-null, the two scales from the maxima (fp32 or bf16 bit patterns).
 hipError_t launch_calibrate(const CalibArgs &a, int32_t sides, void *scales_out, int32_t out_bf16,
                             hipStream_t stream);
-
-hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int32_t n_out, hipStream_t stream);
 
 // ---------------------------------------------------------------- checked mode
 constexpr uint32_t kCheckRepeatedSlot = 1u;   // a slot appears twice in one call
@@ -154,20 +151,5 @@ hipError_t launch_check_slots(uint32_t *w, int64_t bitmap_words, const int64_t *
                               int64_t pool_slots, hipStream_t stream);
 hipError_t launch_check_tables(uint32_t *w, const CheckTablesArgs &a, hipStream_t stream);
 
-struct GatherProbeArgs {
-    const uint8_t *k_pool;   // this layer
-    const uint8_t *v_pool;
-    const int32_t *block_tables;
-    const int32_t *seq_lens;
-    uint32_t *out;           // [num_seqs * kv_heads]
-    int64_t num_blocks;      // pool blocks: table entries are clamped below it
-    int32_t max_blocks;
-    int32_t num_seqs;
-    int32_t kv_heads;
-    int32_t block_size;
-    int32_t k_words_log2;    // log2 of 16-byte words per (block, kv-head) tile
-    int32_t v_words_log2;
-};
-hipError_t launch_gather_probe(const GatherProbeArgs &a, hipStream_t stream);
 
 }  // namespace kvf8

@@ -1,0 +1,51 @@
+/*
+ * Measurement aids for the benchmark, not steps of the cache and not part of
+ * the kvfp8 library: a plain streaming read of a device buffer (the part's
+ * practical read-bandwidth ceiling) and a plain read of exactly the K/V tiles
+ * a paged decode reads (the ceiling of its scattered access pattern).  Built
+ * into libkvf8probe.so.  Every call checks its arguments on the host and
+ * launches nothing when one is wrong; it returns 0 on success, 1 for an
+ * invalid argument (message in kvf8_probe_last_error) and 6 for a HIP error.
+ */
+#ifndef KVF8_PROBE_H
+#define KVF8_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Message of the calling thread's last failed call ("" after a success). */
+const char *kvf8_probe_last_error(void);
+
+/*
+ * Streaming read of `bytes` of device memory at `buf` (16-byte aligned, bytes
+ * a multiple of 16) by n_out workgroups (1 <= n_out <= 2^20), grid-stride;
+ * workgroup i writes the XOR of every 32-bit word it read to out_words[i]
+ * (device, caller-owned), so the XOR of all out_words equals the XOR of the
+ * buffer's 32-bit words.  bytes == 0 is a no-op.  Asynchronous on `stream`.
+ */
+int kvf8_probe_read(const void *buf, size_t bytes, uint32_t *out_words, int32_t n_out, void *stream);
+
+/*
+ * Read of every K and V tile of blocks 0 .. ceil(seq_lens[b] / block_size) - 1
+ * of block_tables[b] (never past max_blocks entries), for every kv-head: the
+ * tiles paged_attn_decode reads.  k_pool / v_pool (device): one layer's pools,
+ * [num_blocks][num_kv_heads][block_size * head_dim] elements of k_elem_bytes /
+ * v_elem_bytes (1 or 2) bytes.  Block ids at or past num_blocks read the last
+ * block.  Workgroup (b, h) writes the XOR of every 32-bit word of its tiles to
+ * out_words[b * num_kv_heads + h] (device, caller-owned).  block_size in
+ * {16, 32}, head_dim in {64, 128, 256}.  Asynchronous on `stream`.
+ */
+int kvf8_probe_gather(const void *k_pool, const void *v_pool, int64_t num_blocks, int32_t num_kv_heads,
+                      int32_t block_size, int32_t head_dim, int32_t k_elem_bytes, int32_t v_elem_bytes,
+                      const int32_t *block_tables, int32_t max_blocks, const int32_t *seq_lens, int32_t num_seqs,
+                      uint32_t *out_words, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVF8_PROBE_H */

@@ -1,0 +1,206 @@
+// kvf8_probe_read: a plain streaming read of a device buffer, the achievable
+// read-bandwidth ceiling that the cache kernels are measured beside.
+//
+// Every workgroup walks the buffer's 16-byte words grid-stride (one load per
+// lane per iteration: more in flight measured slower), XORs everything it
+// read into one 32-bit word and
+// writes it to out[blockIdx.x]; the XOR of all out words is the XOR of every
+// 32-bit word of the buffer, so the result can be checked and the loads
+// cannot be dropped.
+//
+// kvf8_probe_gather: the same plain read, but of exactly the tiles a paged
+// decode reads: workgroup (sequence, kv-head) walks its sequence's K and V
+// tiles through the block table (block ids staged in LDS, four 16-byte loads
+// in flight per lane, K tiles then V tiles) and writes their XOR.  Its rate
+// is the ceiling of the decode's access pattern (scattered tiles), as
+// opposed to a linear stream.  Measurement aids of the benchmark only, built
+// into their own library (libkvf8probe.so), not into the cache library.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "readprobe.h"
+
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+constexpr int kThreads = 256;
+
+struct GatherArgs {
+    const void *k_pool;
+    const void *v_pool;
+    const int32_t *block_tables;
+    const int32_t *seq_lens;
+    uint32_t *out;
+    int64_t num_blocks;
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t kv_heads;
+    int32_t block_size;
+    int32_t k_words_log2;    // log2 of the 16-byte words of one (block, head) tile
+    int32_t v_words_log2;
+};
+
+__global__ __launch_bounds__(kThreads) void read_probe(const u32x4 *buf, int64_t n16, uint32_t *out) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) acc ^= buf[i];
+    uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    for (int o = 32; o > 0; o >>= 1) x ^= (uint32_t)__shfl_xor((int)x, o);
+    __shared__ uint32_t part[kThreads / 64];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+        for (int w = 0; w < kThreads / 64; ++w) r ^= part[w];
+        out[blockIdx.x] = r;
+    }
+}
+
+constexpr int kGatherIds = 4096;   // block ids staged in LDS per pass
+constexpr int kGatherUnroll = 4;   // 16-byte loads in flight per lane
+
+// XOR of the 16-byte words of tiles ids[0..nb) of one kv-head in one pool.
+__device__ __forceinline__ u32x4 gather_words(const u32x4 *pool, const int32_t *ids, int nb, int wl, int head,
+                                              int heads) {
+    const int64_t words = (int64_t)nb << wl;
+    const int64_t mask = ((int64_t)1 << wl) - 1;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int64_t w = threadIdx.x; w < words; w += kGatherUnroll * kThreads) {
+        u32x4 x[kGatherUnroll];
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            const int64_t ww = w + u * kThreads;
+            x[u] = u32x4{0u, 0u, 0u, 0u};
+            if (ww < words) {
+                const int64_t tile = (int64_t)ids[ww >> wl] * heads + head;
+                x[u] = pool[(tile << wl) + (ww & mask)];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) acc ^= x[u];
+    }
+    return acc;
+}
+
+__global__ __launch_bounds__(kThreads) void gather_probe(GatherArgs a) {
+    __shared__ int32_t ids[kGatherIds];
+    const int unit = blockIdx.x;
+    const int seq = unit / a.kv_heads, head = unit - seq * a.kv_heads;
+    const int len = a.seq_lens[seq];
+    int64_t nblk = len > 0 ? (len + a.block_size - 1) / a.block_size : 0;
+    if (nblk > a.max_blocks) nblk = a.max_blocks;            // as the decode: never past the table row
+    const int32_t *table = a.block_tables + (int64_t)seq * a.max_blocks;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int64_t b0 = 0; b0 < nblk; b0 += kGatherIds) {
+        const int nb = (int)(nblk - b0 < kGatherIds ? nblk - b0 : kGatherIds);
+        __syncthreads();
+        for (int i = threadIdx.x; i < nb; i += kThreads) {
+            const uint32_t id = (uint32_t)table[b0 + i];          // out-of-pool ids read the last block
+            ids[i] = (int32_t)(id < a.num_blocks ? id : (uint32_t)(a.num_blocks - 1));
+        }
+        __syncthreads();
+        acc ^= gather_words(reinterpret_cast<const u32x4 *>(a.k_pool), ids, nb, a.k_words_log2, head, a.kv_heads);
+        acc ^= gather_words(reinterpret_cast<const u32x4 *>(a.v_pool), ids, nb, a.v_words_log2, head, a.kv_heads);
+    }
+    uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    for (int o = 32; o > 0; o >>= 1) x ^= (uint32_t)__shfl_xor((int)x, o);
+    __shared__ uint32_t part[kThreads / 64];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+        for (int w = 0; w < kThreads / 64; ++w) r ^= part[w];
+        a.out[unit] = r;
+    }
+}
+
+thread_local std::string g_last_error;
+
+int fail(const char *fmt, ...) {
+    char buf[256];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return 1;
+}
+
+int launched(const char *what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        fail("%s: %s", what, hipGetErrorString(e));
+        return 6;
+    }
+    g_last_error.clear();
+    return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvf8_probe_last_error(void) { return g_last_error.c_str(); }
+
+int kvf8_probe_read(const void *buf, size_t bytes, uint32_t *out_words, int32_t n_out, void *stream) {
+    if (bytes == 0) {
+        g_last_error.clear();
+        return 0;
+    }
+    if (!buf || !out_words) return fail("buf and out_words must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(buf) % 16) != 0 || bytes % 16 != 0)
+        return fail("buf must be 16-byte aligned and bytes a multiple of 16");
+    if (n_out < 1 || n_out > (1 << 20)) return fail("n_out must be in [1, 2^20]");
+    hipLaunchKernelGGL(read_probe, dim3((unsigned)n_out), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4 *>(buf), (int64_t)(bytes / 16), out_words);
+    return launched("kvf8_probe_read launch");
+}
+
+int kvf8_probe_gather(const void *k_pool, const void *v_pool, int64_t num_blocks, int32_t num_kv_heads,
+                      int32_t block_size, int32_t head_dim, int32_t k_elem_bytes, int32_t v_elem_bytes,
+                      const int32_t *block_tables, int32_t max_blocks, const int32_t *seq_lens, int32_t num_seqs,
+                      uint32_t *out_words, void *stream) {
+    if (num_seqs < 0 || max_blocks < 0) return fail("num_seqs and max_blocks must be >= 0");
+    if (num_blocks <= 0 || num_kv_heads <= 0) return fail("num_blocks and num_kv_heads must be positive");
+    if ((block_size != 16 && block_size != 32) || (head_dim != 64 && head_dim != 128 && head_dim != 256))
+        return fail("block_size must be 16 or 32 and head_dim 64, 128 or 256");
+    if ((k_elem_bytes != 1 && k_elem_bytes != 2) || (v_elem_bytes != 1 && v_elem_bytes != 2))
+        return fail("element bytes must be 1 or 2");
+    if (num_seqs == 0) {
+        g_last_error.clear();
+        return 0;
+    }
+    if (!k_pool || !v_pool || !block_tables || !seq_lens || !out_words)
+        return fail("pools, block_tables, seq_lens and out_words must be non-NULL");
+    if ((int64_t)num_seqs * num_kv_heads > 0x7FFFFFFF) return fail("too many (sequence, kv-head) units");
+    auto words_log2 = [&](int eb) {
+        const int64_t words = (int64_t)block_size * head_dim * eb / 16;
+        int l = 0;
+        while ((int64_t(1) << l) < words) ++l;
+        return l;
+    };
+    GatherArgs a{};
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.out = out_words;
+    a.num_blocks = num_blocks;
+    a.max_blocks = max_blocks;
+    a.num_seqs = num_seqs;
+    a.kv_heads = num_kv_heads;
+    a.block_size = block_size;
+    a.k_words_log2 = words_log2(k_elem_bytes);
+    a.v_words_log2 = words_log2(v_elem_bytes);
+    hipLaunchKernelGGL(gather_probe, dim3((unsigned)(num_seqs * num_kv_heads)), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), a);
+    return launched("kvf8_probe_gather launch");
+}
+
+}  // extern "C"

@@ -124,7 +124,7 @@ def test_decode_ring_is_sound_in_every_e4m3_instance(tmp_path):
         pytest.skip("hipcc not available")
     src = os.path.join(ROOT, "fp8_e4m3_scaled_amd", "csrc", "decode.hip")
     out = tmp_path / "decode.s"
-    flags = [f for f in cflags if f != "-fPIC"]
+    flags = [f for f in cflags if f not in ("-fPIC", "-Werror")]   # -S: hipcc adds an unused --hip-link
     r = subprocess.run([hipcc, *flags, "--cuda-device-only", "-S", src, "-o", str(out)],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr

@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import fp8_e4m3_scaled_amd as kv
+import probe
 from tests.gpu_util import DEV, log
 
 pytestmark = pytest.mark.gpu
@@ -20,7 +21,7 @@ def test_read_probe_xor(nbytes, n_out):
     host = rng.integers(0, 1 << 32, size=nbytes // 4, dtype=np.uint32)
     buf = torch.from_numpy(host.view(np.int32)).to(DEV)
     out = torch.full((n_out,), -1, dtype=torch.int32, device=DEV)
-    kv.kvf8_read_probe(buf, nbytes, out, n_out)
+    probe.read(buf, nbytes, out, n_out)
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
     assert int(got) == int(np.bitwise_xor.reduce(host))
@@ -43,15 +44,11 @@ def test_gather_probe_xor(BS, Hkv, D, v_elem):
     vp = rng.integers(0, 1 << 32, size=NB * Hkv * tile_v // 4, dtype=np.uint32)
     k_dev = torch.from_numpy(kp.view(np.int32)).to(DEV)
     v_dev = torch.from_numpy(vp.view(np.int32)).to(DEV)
-    h = kv.kv_cache_alloc_typed(1, NB, BS, Hkv, D, kv.ELEM_E4M3, v_elem, [1.0], [1.0], kv.DTYPE_F32, k_dev, v_dev)
-    try:
-        out = torch.full((lens.size * Hkv,), -1, dtype=torch.int32, device=DEV)
-        kv.kvf8_gather_probe(h, 0, torch.from_numpy(tables).to(DEV), max_blocks, torch.from_numpy(lens).to(DEV),
-                             lens.size, out)
-        torch.cuda.synchronize()
-        got = out.cpu().numpy().view(np.uint32)
-    finally:
-        kv.kv_cache_free(h)
+    out = torch.full((lens.size * Hkv,), -1, dtype=torch.int32, device=DEV)
+    probe.gather(k_dev, v_dev, NB, Hkv, BS, D, 1, veb, torch.from_numpy(tables).to(DEV), max_blocks,
+                 torch.from_numpy(lens).to(DEV), lens.size, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32)
     kt = kp.reshape(NB, Hkv, tile_k // 4)
     vt = vp.reshape(NB, Hkv, tile_v // 4)
     for b, L in enumerate(lens):
