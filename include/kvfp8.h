@@ -409,33 +409,6 @@ kvf8_status kv_calibrate_scales(const uint16_t *k_bf16, const uint16_t *v_bf16, 
                                 int64_t v_tok_stride, int64_t num_tokens, int64_t row_elems, float *amax,
                                 void *scales_out, kvf8_dtype scale_dtype, void *stream);
 
-/*
- * Measurement aid, not a step of the cache: a plain streaming read of `bytes`
- * of device memory at `buf` (16-byte aligned, bytes a multiple of 16), the
- * achievable read-bandwidth ceiling that the cache kernels are reported
- * beside.  n_out workgroups (1 <= n_out <= 2^20) read the buffer grid-stride;
- * workgroup i writes the XOR of every 32-bit word it read to out_words[i]
- * (device, n_out words, caller-owned), so the XOR of all out_words equals the
- * XOR of the buffer's 32-bit words.  Asynchronous on `stream`.
- */
-kvf8_status kvf8_read_probe(const void *buf, size_t bytes, uint32_t *out_words, int32_t n_out,
-                            void *stream);
-
-/*
- * Measurement aid, not a step of the cache: a plain read of exactly the K and
- * V tiles paged_attn_decode reads for these sequences (every tile of blocks
- * 0 .. ceil(seq_lens[b] / block_size) - 1 of block_tables[b], for every
- * kv-head), the ceiling of the decode's scattered-tile access pattern.
- * Workgroup (b, kv-head h) writes the XOR of every 32-bit word of its K and V
- * tiles to out_words[b * num_kv_heads + h] (device, caller-owned).
- * block_tables, seq_lens (device) as in paged_attn_decode; as there, block
- * ids at or past num_blocks read the last block and a sequence never reads
- * past its max_blocks table entries.  Asynchronous on `stream`.
- */
-kvf8_status kvf8_gather_probe(const kvf8_cache *cache, int32_t layer, const int32_t *block_tables,
-                              int32_t max_blocks, const int32_t *seq_lens, int32_t num_seqs,
-                              uint32_t *out_words, void *stream);
-
 #ifdef __cplusplus
 }
 #endif
