@@ -159,6 +159,11 @@ def run_llama8b(args):
     st_t = _timed(store, args.steps, args.warmup, stream)
     de_t = _timed(decode, args.steps, args.warmup, stream)
     wall = time.perf_counter() - t0
+    # the same decode with fp32 outputs (untimed), for the parity sample
+    out_f32 = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
+    kv.paged_attn_decode(handles[0], 0, q, w.Hq, tables, w.max_blocks, lens, w.B, max_len, w.sm_scale(), out_f32,
+                         kv.DTYPE_F32, ws, ws_bytes, stream)
+    torch.cuda.synchronize()
 
     # algorithmic bytes (what the method must move)
     kv_bytes = int(w.total_lengths.sum()) * 2 * w.Hkv * w.D
@@ -218,8 +223,13 @@ def run_llama8b(args):
     result["element_types"] = _typed_exchange(args, kv, w, K, V, slots_d, T, q, tables, lens, max_len, out,
                                               ks, vs, de_mean, stream)
     if args.cpu_seconds > 0:
-        result["cpu_baseline"], result["parity_sample"] = _cpu_baseline(
-            w, K, V, slots, q, out, ks, vs, args.cpu_seconds)
+        offs = np.concatenate([[0], np.cumsum(w.total_lengths)]).astype(np.int64)
+        oh = OracleHost(w, range(w.B), w.block_tables, w.total_lengths, ks, vs,
+                        lambda b, lo, n: (K[offs[b] + lo:offs[b] + lo + n], V[offs[b] + lo:offs[b] + lo + n]))
+        got = {"bf16": out.float().cpu().numpy(), "fp32": out_f32.cpu().numpy()}
+        cpu_de, result["parity_sample"] = _cpu_decode(w, oh, q, got, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_de
+        result["cpu_baseline_ops"] = {"decode": cpu_de, "store": _cpu_store(w, oh, args.cpu_seconds / 2)}
     return result
 
 
@@ -342,14 +352,16 @@ def _timed_oracle(items, fn, budget_s):
     oracle releases the GIL) on the next items.  Returns the per-item results,
     the two (items, seconds) pairs and the thread count."""
     from concurrent.futures import ThreadPoolExecutor
+    n = _host_threads()
+    # leave at least as many items for every core as the single thread takes
+    max_single = max(1, len(items) // (n + 1))
     results, single_t, i = [], 0.0, 0
-    while i < len(items) and single_t < budget_s / 2:
+    while i < min(len(items), max_single) and single_t < budget_s / 2:
         t0 = time.perf_counter()
         results.append(fn(items[i]))
         single_t += time.perf_counter() - t0
         i += 1
     single_n = i
-    n = _host_threads()
     per_thread = max(1, single_n)
     batch = items[i:i + n * per_thread]
     t0 = time.perf_counter()
@@ -359,60 +371,165 @@ def _timed_oracle(items, fn, budget_s):
     return results, (single_n, single_t), (len(batch), multi_t), n
 
 
-def _cpu_baseline(w, K, V, slots, q, out, ks, vs, budget_s):
-    """The CPU oracle on a bounded sample: (sequence, kv-head) groups in a seeded
-    order, all query heads of each group, one thread and then all host cores.
-    Also compares the GPU decode output on those heads with the oracle (the
-    same tolerance as the tests)."""
+class OracleHost:
+    """Host pools of the CPU oracle holding every token of the sequences `seqs`
+    (stored by the oracle itself, untimed), in compact block ids: the blocks the
+    sequences use, renumbered 0.. in table order, so that a pool of any size on
+    the GPU (the variable-length workload's is 144 GB) needs only the sampled
+    sequences' blocks on the host.  src(b, lo, n) gives the bf16 K/V rows."""
+
+    def __init__(self, w, seqs, tables, lens, ks, vs, src):
+        import oracle
+        from concurrent.futures import ThreadPoolExecutor
+        oracle._load()
+        self.w, self.ks, self.vs, self.lens = w, np.float32(ks), np.float32(vs), np.asarray(lens, np.int64)
+        self.seqs = list(seqs)
+        self.tables = np.zeros_like(tables)
+        nb = 0
+        for b in self.seqs:
+            n = -(-int(self.lens[b]) // w.BS)
+            self.tables[b, :n] = np.arange(nb, nb + n, dtype=np.int32)
+            nb += n
+        self.kp = np.zeros((max(1, nb), w.Hkv, w.BS * w.D), np.uint8)
+        self.vp = np.zeros_like(self.kp)
+        self.src = src
+        step = 16384
+
+        def one(b):
+            L = int(self.lens[b])
+            for lo in range(0, L, step):
+                n = min(step, L - lo)
+                k, v = self.rows(b, lo, n)
+                oracle.store(k, v, self.slots(b, lo, n), self.kp, self.vp, Hkv=w.Hkv, D=w.D, BS=w.BS,
+                             k_scale=self.ks, v_scale=self.vs)
+        with ThreadPoolExecutor(max_workers=_host_threads()) as ex:
+            list(ex.map(one, self.seqs))
+
+    def rows(self, b, lo, n):
+        from synth import bf16_bits
+        k, v = self.src(b, lo, n)
+        row = self.w.Hkv * self.w.D
+        return bf16_bits(k).reshape(n, row), bf16_bits(v).reshape(n, row)
+
+    def slots(self, b, lo, n):
+        p = np.arange(lo, lo + n, dtype=np.int64)
+        return self.tables[b, p // self.w.BS].astype(np.int64) * self.w.BS + p % self.w.BS
+
+
+def _cpu_decode(w, oh, q, got, budget_s):
+    """The oracle's decode on a bounded sample: (sequence, kv-head) groups of the
+    host pools' sequences in a seeded order, all query heads of each group, one
+    thread and then all host cores.  Also compares the GPU decode outputs on
+    those heads with the oracle: got maps "bf16" / "fp32" to [B][Hq][D] outputs;
+    every element within |d| <= 2e-3 + 1e-2 |ref|, and the fp32 output's max |d|
+    reported beside 2e-3."""
     import oracle
     from synth import bf16_bits
-    oracle._load()
     q_bits = bf16_bits(q)
-    got = out.float().cpu().numpy()
     G = w.Hq // w.Hkv
-    row = w.Hkv * w.D
+    lens = oh.lens.astype(np.int32)
     rng = np.random.default_rng(7)
-    order = [(int(i // w.Hkv), int(i % w.Hkv)) for i in rng.permutation(w.B * w.Hkv)]
-    kp = np.zeros((w.NB, w.Hkv, w.BS * w.D), np.uint8)
-    vp = np.zeros_like(kp)
-    offs = np.concatenate([[0], np.cumsum(w.total_lengths)])
-    lens = w.total_lengths.astype(np.int32)
-    # the oracle reads only bytes it stored itself; stores are outside the timed calls
-    n_max = len(order)
-    for b in sorted({b for b, _ in order[:n_max]}):
-        lo, hi = int(offs[b]), int(offs[b + 1])
-        oracle.store(bf16_bits(K[lo:hi]).reshape(hi - lo, row), bf16_bits(V[lo:hi]).reshape(hi - lo, row),
-                     slots[lo:hi], kp, vp, Hkv=w.Hkv, D=w.D, BS=w.BS, k_scale=ks, v_scale=vs)
+    order = [(b, h) for b in oh.seqs for h in rng.permutation(w.Hkv).tolist()]
 
     def group(item):
         b, kvh = item
         sel = np.array([[b, kvh * G + j] for j in range(G)], np.int32)
-        ref = oracle.decode_attn(q_bits, kp, vp, w.block_tables, lens, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
-                                 BS=w.BS, k_scale=ks, v_scale=vs, sm_scale=w.sm_scale(), sel=sel)
+        ref = oracle.decode_attn(q_bits, oh.kp, oh.vp, oh.tables, lens, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
+                                 BS=w.BS, k_scale=oh.ks, v_scale=oh.vs, sm_scale=w.sm_scale(), sel=sel)
         # a copy: the view would keep the oracle's whole [B][Hq][D] output alive
         return item, ref[b, kvh * G:(kvh + 1) * G].copy()
 
     def nbytes(item):
-        L = int(w.total_lengths[item[0]])
+        L = int(lens[item[0]])
         return L * 2 * w.D + G * w.D * (2 + 2) + 4 * (-(-L // w.BS)) + 4
 
     results, (n1, t1), (n2, t2), threads = _timed_oracle(order, group, budget_s)
-    worst, bad = 0.0, 0
-    for (b, kvh), ref in results:
-        g = got[b, kvh * G:(kvh + 1) * G]
-        err = np.abs(g - ref)
-        worst = max(worst, float(err.max()))
-        bad += int((err > 2e-3 + 1e-2 * np.abs(ref)).sum())
+    parity = {"heads_checked": len(results) * G}
+    for name, g in got.items():
+        worst, bad = 0.0, 0
+        for (b, kvh), ref in results:
+            err = np.abs(g[b, kvh * G:(kvh + 1) * G] - ref)
+            worst = max(worst, float(err.max()))
+            bad += int((err > 2e-3 + 1e-2 * np.abs(ref)).sum())
+        parity[f"max_abs_err_{name}_out"] = worst
+        parity[f"outside_tolerance_{name}_out"] = bad
     b1 = sum(nbytes(it) for it, _ in results[:n1])
     b2 = sum(nbytes(it) for it, _ in results[n1:])
     cpu = {"value": round(b2 / t2 / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
            "sample": f"{n2} (sequence, kv-head) groups x {G} query heads on {threads} threads, fp64 C "
-                     f"oracle, {t2:.1f} s wall (seeded order over all {w.B * w.Hkv} groups)",
+                     f"oracle, {t2:.1f} s wall (seeded order over {len(order)} groups)",
            "single_thread": {"value": round(b1 / t1 / 1e9, 4), "cores": 1,
                              "sample": f"{n1} groups, {t1:.1f} s"},
            "tokens_per_s": round(n2 * G / w.Hq / t2, 4)}
-    parity = {"heads_checked": len(results) * G, "max_abs_err_bf16_out": worst, "outside_tolerance": bad}
     return cpu, parity
+
+
+def _cpu_store(w, oh, budget_s, chunk=2048):
+    """The oracle's store on a bounded sample: chunks of `chunk` tokens of the
+    host pools' sequences (their rows drawn before the timed calls), one thread
+    and then all host cores; chunks write disjoint slots.  Rewriting a token
+    writes the bytes it already holds."""
+    import oracle
+    items = []
+    for b in oh.seqs:
+        for lo in range(0, int(oh.lens[b]), chunk):
+            items.append((b, lo, min(chunk, int(oh.lens[b]) - lo)))
+    rng = np.random.default_rng(8)
+    items = [items[i] for i in rng.permutation(len(items))[:max(1, min(len(items), 16 * 32))]]
+    rows = {}
+
+    def prepare(it):
+        if it not in rows:
+            rows[it] = oh.rows(*it)
+        return rows[it]
+
+    def one(it):
+        k, v = rows[it]
+        b, lo, n = it
+        oracle.store(k, v, oh.slots(b, lo, n), oh.kp, oh.vp, Hkv=w.Hkv, D=w.D, BS=w.BS, k_scale=oh.ks,
+                     v_scale=oh.vs)
+        return n
+
+    # inputs of the first items (eight per host core), drawn outside the timed calls
+    for it in items[:8 * (_host_threads() + 1)]:
+        prepare(it)
+    items = [it for it in items if it in rows]
+    results, (n1, t1), (n2, t2), threads = _timed_oracle(items, one, budget_s)
+    tok1, tok2 = sum(results[:n1]), sum(results[n1:])
+    per_tok = 6 * w.Hkv * w.D + 8
+    return {"value": round(tok2 / t2, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "GBps": round(tok2 * per_tok / t2 / 1e9, 4),
+            "sample": f"{n2} chunks of up to {chunk} tokens on {threads} threads, C oracle, {t2:.2f} s wall",
+            "single_thread": {"value": round(tok1 / t1, 1), "cores": 1, "GBps": round(tok1 * per_tok / t1 / 1e9, 4),
+                              "sample": f"{n1} chunks, {t1:.2f} s"}}
+
+
+def _cpu_kshift(w, oh, delta, theta, rot, budget_s, chunk=4096):
+    """The oracle's K-shift (fp64 rotation, NEOX) on a bounded sample: chunks of
+    `chunk` slots of the host pools' sequences, one thread and then all host
+    cores (disjoint slots).  Runs in place on the host pools."""
+    import oracle
+    items = []
+    for b in oh.seqs:
+        for lo in range(0, int(oh.lens[b]), chunk):
+            items.append((b, lo, min(chunk, int(oh.lens[b]) - lo)))
+    rng = np.random.default_rng(9)
+    items = [items[i] for i in rng.permutation(len(items))]
+
+    def one(it):
+        b, lo, n = it
+        oracle.kshift(oh.kp, oh.slots(b, lo, n), Hkv=w.Hkv, D=w.D, BS=w.BS, delta=delta, theta=theta,
+                      rot_dim=rot, neox=True)
+        return n
+
+    results, (n1, t1), (n2, t2), threads = _timed_oracle(items, one, budget_s)
+    s1, s2 = sum(results[:n1]), sum(results[n1:])
+    per_slot = 2 * w.Hkv * rot + 8
+    return {"value": round(s2 * per_slot / t2 / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "slots_per_s": round(s2 / t2, 1),
+            "sample": f"{n2} chunks of up to {chunk} slots on {threads} threads, C oracle, {t2:.2f} s wall",
+            "single_thread": {"value": round(s1 * per_slot / t1 / 1e9, 4), "cores": 1,
+                              "sample": f"{n1} chunks, {t1:.2f} s"}}
 
 
 def _fill(w, kv, dev, stream, copies=1, upto=None, empty=False, elems=None):
@@ -554,7 +671,11 @@ def run_prefill(args):
                        "traffic": _traffic_from_profile("prefill_pmc.txt", psha),
                        "kernel": "prefill_kernel<128,16,1,1>", "kernel_source_sha": psha}
     if args.cpu_seconds > 0:
-        res["cpu_baseline"] = _cpu_prefill(w, q, out, ctx, n, args.cpu_seconds)
+        ks_, vs_, _ = w.scales()
+        oh = OracleHost(w, range(w.B), w.block_tables, w.total_lengths, ks_, vs_,
+                        lambda b, lo, m: w.kv(b, lo, m, device=dev))
+        res["cpu_baseline"] = _cpu_prefill(w, oh, q, out, ctx, n, args.cpu_seconds)
+        res["cpu_baseline_ops"] = {"prefill": res["cpu_baseline"], "store": _cpu_store(w, oh, args.cpu_seconds / 2)}
     kv.kv_cache_free(h)
     del pools
     # The same prefill over the bf16 twin and the mixed caches (context and
@@ -581,24 +702,12 @@ def run_prefill(args):
     return res
 
 
-def _cpu_prefill(w, q, out, ctx, n, budget_s):
+def _cpu_prefill(w, oh, q, out, ctx, n, budget_s):
     """Oracle FLOP/s on sampled query rows, one thread and then all host cores
-    (and the rows' parity with the GPU output)."""
+    (and the rows' parity with the GPU output); oh holds every sequence."""
     import oracle
     from synth import bf16_bits
-    oracle._load()
-    # the oracle reads bytes that it stored itself: store every sequence again on the CPU
-    okp = np.zeros((w.NB, w.Hkv, w.BS * w.D), np.uint8)
-    ovp = np.zeros_like(okp)
-    row = w.Hkv * w.D
-    ks, vs, _ = w.scales()
-    for b in range(w.B):
-        L = int(w.total_lengths[b])
-        for lo in range(0, L, 8192):
-            m = min(8192, L - lo)
-            k, v = w.kv(b, lo, m, device=q.device)
-            oracle.store(bf16_bits(k).reshape(m, row), bf16_bits(v).reshape(m, row), w.slots(b, lo, m),
-                         okp, ovp, Hkv=w.Hkv, D=w.D, BS=w.BS, k_scale=ks, v_scale=vs)
+    okp, ovp, ks, vs = oh.kp, oh.vp, oh.ks, oh.vs
     qb = bf16_bits(q)
     got = out.float().cpu().numpy()
     cu = (np.arange(w.B + 1) * n).astype(np.int32)
@@ -611,7 +720,7 @@ def _cpu_prefill(w, q, out, ctx, n, budget_s):
     calls = [rows[i:i + per_call] for i in range(0, len(rows), per_call)]
 
     def one(call):
-        ref = oracle.prefill_attn(qb, okp, ovp, cu, ctx, w.block_tables, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
+        ref = oracle.prefill_attn(qb, okp, ovp, cu, ctx, oh.tables, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
                                   BS=w.BS, k_scale=ks, v_scale=vs, sm_scale=w.sm_scale(),
                                   sel=np.array(call, np.int64))
         return [((r, hh), ref[r, hh].copy()) for r, hh in call]
@@ -675,6 +784,15 @@ def run_longctx(args):
         kv.kv_shift_rope_per_slot(handles[i % copies], 0, slots, rows, nsl, table, w.B, w.D, kv.ROPE_NEOX,
                                   stream)
 
+    # outputs for the parity sample, before the timed shifts turn the cached keys
+    got = {}
+    if args.cpu_seconds > 0:
+        for name, dt, tdt in (("bf16", kv.DTYPE_BF16, torch.bfloat16), ("fp32", kv.DTYPE_F32, torch.float32)):
+            o = torch.empty((w.B, w.Hq, w.D), dtype=tdt, device=dev)
+            kv.paged_attn_decode(handles[0], 0, q, w.Hq, tables, w.max_blocks, lens_d, w.B, max_len,
+                                 w.sm_scale(), o, dt, ws, ws_bytes, stream)
+            torch.cuda.synchronize()
+            got[name] = o.float().cpu().numpy()
     de = _timed(decode, args.steps, args.warmup, stream)
     sh = _timed(shift, args.steps, args.warmup, stream)
     sp = _timed(shift_per_slot, args.steps, args.warmup, stream)
@@ -704,6 +822,16 @@ def run_longctx(args):
                        "kernel": "decode_kernel<256,32,1,1> + decode_reduce<256>", "kernel_source_sha": dsha}
     for h in handles:
         kv.kv_cache_free(h)
+    del pools
+    torch.cuda.empty_cache()
+    if args.cpu_seconds > 0:
+        ks, vs, _ = w.scales()
+        oh = OracleHost(w, range(w.B), w.block_tables, lens, ks, vs, lambda b, lo, n: w.kv(b, lo, n, device=dev))
+        cpu_de, res["parity_sample"] = _cpu_decode(w, oh, q, got, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_de
+        res["cpu_baseline_ops"] = {"decode": cpu_de, "store": _cpu_store(w, oh, args.cpu_seconds / 2),
+                                   "kv_shift": _cpu_kshift(w, oh, w.spec.delta, w.spec.theta, w.D,
+                                                           args.cpu_seconds / 2)}
     return res
 
 
@@ -716,10 +844,26 @@ def run_varlen(args):
     import fp8_e4m3_scaled_amd as kv
     from synth import Workload
     dev, stream = torch.device("cuda:0"), torch.cuda.current_stream()
+    from synth import f32_to_bf16_bits
     w = Workload("varlen", device=dev, pool_frac=args.pool_frac)
-    pools, handles = _fill(w, kv, dev, stream, empty=True)
-    h = handles[0]
+    # The pool (its contents are never read outside the stored tokens), the
+    # scales as bf16 bit patterns (KVF8_DTYPE_BF16), and block tables drawn by
+    # the library's allocator from a shuffled free list over the whole pool.
+    ks, vs, _ = w.scales()
+    kp = torch.empty((w.NB, w.Hkv, w.BS * w.D), dtype=torch.uint8, device=dev)
+    vp = torch.empty_like(kp)
+    h = kv.kv_cache_alloc(1, w.NB, w.BS, w.Hkv, w.D, [f32_to_bf16_bits(float(ks))], [f32_to_bf16_bits(float(vs))],
+                          kv.DTYPE_BF16, kp, vp)
+    w.block_tables = _library_tables(kv, h, w, 1003)
     row = w.Hkv * w.D
+    for b in range(w.B):
+        Lb = int(w.lengths[b])
+        for lo in range(0, Lb, 65536):
+            n = min(65536, Lb - lo)
+            k, v = w.kv(b, lo, n, device=dev)
+            kv.kv_store_fp8(h, 0, k.reshape(n, row), v.reshape(n, row), row, row,
+                            torch.from_numpy(w.slots(b, lo, n)).to(dev), n, stream)
+    torch.cuda.synchronize()
     L = w.lengths
     K = torch.cat([w.kv(b, int(L[b]), 1, device=dev)[0].reshape(1, row) for b in range(w.B)])
     V = torch.cat([w.kv(b, int(L[b]), 1, device=dev)[1].reshape(1, row) for b in range(w.B)])
@@ -742,13 +886,17 @@ def run_varlen(args):
 
     st = _timed(store, args.steps, args.warmup, stream)
     de = _timed(decode, args.steps, args.warmup, stream)
+    out_f32 = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
+    kv.paged_attn_decode(h, 0, q, w.Hq, tables, w.max_blocks, lens_d, w.B, max_len, w.sm_scale(), out_f32,
+                         kv.DTYPE_F32, ws, ws_bytes, stream)
+    torch.cuda.synchronize()
     de_bytes = _decode_bytes(w, lens, 2)
     de_gbps = de_bytes / (de.mean() * 1e-3) / 1e9
     res = _header(args, "varlen", round(de_gbps, 1), "GB/s", float(st.mean() + de.mean()),
                   {"q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D, "block_size": w.BS,
                    "num_seqs": w.B, "max_seq_len": max_len, "mean_seq_len": float(lens.mean()),
                    "pool_blocks": int(w.NB), "pool_frac_of_288GB": args.pool_frac, "scale_dtype": "bf16",
-                   "out_dtype": "bf16"})
+                   "tables": "kv_block_shuffle + kv_block_alloc", "out_dtype": "bf16"})
     res["decode"] = dict(_stats(de), algorithmic_bytes=de_bytes, GBps=round(de_gbps, 1),
                          frac_hbm_peak=round(de_gbps / HBM_PEAK_GBPS, 4),
                          tokens_per_s=round(w.B / (de.mean() * 1e-3), 1))
@@ -768,7 +916,29 @@ def run_varlen(args):
                                                   kv_bytes, stream)
     res["decode"]["speedup_over_unsplit_gather"] = round(de_gbps / res["paged_gather_unsplit"]["GBps"], 4)
     kv.kv_cache_free(h)
+    del kp, vp
+    torch.cuda.empty_cache()
+    if args.cpu_seconds > 0:
+        # the oracle holds the blocks of a seeded sample of the sequences (ids remapped)
+        seqs = sorted(np.random.default_rng(12).choice(w.B, 24, replace=False).tolist())
+        oh = OracleHost(w, seqs, w.block_tables, w.total_lengths, ks, vs, lambda b, lo, n: w.kv(b, lo, n, device=dev))
+        got = {"bf16": out.float().cpu().numpy(), "fp32": out_f32.cpu().numpy()}
+        cpu_de, res["parity_sample"] = _cpu_decode(w, oh, q, got, args.cpu_seconds)
+        res["parity_sample"]["sequences"] = f"{len(seqs)} seeded sequences of {w.B}, ids as drawn from the {w.NB}-block pool"
+        res["cpu_baseline"] = cpu_de
+        res["cpu_baseline_ops"] = {"decode": cpu_de, "store": _cpu_store(w, oh, args.cpu_seconds / 2)}
     return res
+
+
+def _library_tables(kv, handle, w, seed):
+    """Block tables from the library's allocator: the free list shuffled with
+    kv_block_shuffle(seed), then kv_block_alloc of each sequence's blocks."""
+    kv.kv_block_shuffle(handle, seed)
+    tables = np.zeros((w.B, w.max_blocks), np.int32)
+    for b in range(w.B):
+        n = -(-int(w.total_lengths[b]) // w.BS)
+        tables[b, :n] = kv.kv_block_alloc(handle, n)
+    return tables
 
 
 def main():

@@ -2,12 +2,13 @@
 
 Every workload is stored and computed on the GPU exactly as the benchmark does
 it (the same store calls, one decode / prefill launch over the whole batch,
-the same split plan, bf16 outputs).  The oracle stores every sequence's own
+the same split plan and pool), with bf16 and fp32 outputs.  The oracle stores every sequence's own
 bf16 K/V into full-size host pools with the same block tables (inputs come
 from the seeded generators on the GPU and reach both sides as the same bf16
 bits; no expected value comes from the HIP library), and
   * the whole K and V pools must equal the oracle's bit for bit;
-  * attention outputs satisfy |gpu - oracle| <= 2e-3 + 1e-2 |oracle|:
+  * attention outputs satisfy |gpu - oracle| <= 2e-3 + 1e-2 |oracle|, and
+    fp32 outputs max |gpu - oracle| <= 2e-3:
     every (sequence, head) of the Llama-shaped decode (E4M3 and its bf16
     twin) and of the variable-length decode and
     of both long-context decodes, and 8,192 prefill (query, head) rows that
@@ -188,30 +189,98 @@ def test_llama8b_full_size(elems):
         cache.close()
 
 
+class _Handle:
+    def __init__(self, h):
+        self.handle = h
+
+
 def test_varlen_full_size():
-    """256 sequences with lengths in [512, 32768] (+1 new token), bf16 scales,
-    8 splits + reduce; all 8.7 GB of cache bytes and all 8,192 heads."""
-    w = Workload("varlen", device=DEV, pool_frac=0.0)    # compact pool; same launch shapes
-    cache = FullCache(w)
+    """256 sequences with lengths in [512, 32768] (+1 new token) over the
+    benchmark's own pool, 50 % of 288 GB (4.39 M blocks): block tables drawn by
+    the library's allocator (kv_block_shuffle, then kv_block_alloc per
+    sequence), scales given as bf16 bit patterns (KVF8_DTYPE_BF16), 8 splits +
+    reduce.  Every byte of every block in use and all 8,192 heads against the
+    oracle, which holds those blocks under compact ids (the same bytes, 8.7 GB
+    instead of the pool's 144 GB)."""
+    from synth import f32_to_bf16_bits
+    w = Workload("varlen", device=DEV)
+    ks, vs, sdt = w.scales()
+    assert sdt == "bf16" and w.NB > 4_000_000
+    k_pool = torch.zeros((w.NB, w.Hkv, w.BS * w.D), dtype=torch.uint8, device=DEV)
+    v_pool = torch.zeros_like(k_pool)
+    h = kv.kv_cache_alloc(1, w.NB, w.BS, w.Hkv, w.D, [f32_to_bf16_bits(float(ks))], [f32_to_bf16_bits(float(vs))],
+                          kv.DTYPE_BF16, k_pool, v_pool)
     try:
-        log(f"varlen full: fill {int(w.lengths.sum())} tokens, store 1 token x {w.B}, decode")
-        cache.fill(w.lengths)
+        assert kv.kv_cache_get_scales(h, 0) == (float(ks), float(vs))     # the bf16 bits, widened exactly
+        kv.kv_block_shuffle(h, 1003)
+        nblk = [-(-int(L) // w.BS) for L in w.total_lengths]
+        tables = np.zeros((w.B, w.max_blocks), np.int32)
+        for b in range(w.B):
+            tables[b, :nblk[b]] = kv.kv_block_alloc(h, nblk[b])
+        assert kv.kv_blocks_free(h) == w.NB - sum(nblk)
+        assert tables.max() > w.NB // 2                          # scattered over the whole pool
+        w.block_tables = tables
         row = w.Hkv * w.D
+        log(f"varlen full on the {w.NB}-block pool: fill {int(w.lengths.sum())} tokens, store 1 x {w.B}, decode")
+        for b in range(w.B):
+            L = int(w.lengths[b])
+            for lo in range(0, L, FILL_STEP):
+                n = min(FILL_STEP, L - lo)
+                k, v = w.kv(b, lo, n, device=DEV)
+                kv.kv_store_fp8(h, 0, k.reshape(n, row), v.reshape(n, row), row, row, t_dev(w.slots(b, lo, n)), n)
         L = w.lengths
         K = torch.cat([w.kv(b, int(L[b]), 1, device=DEV)[0].reshape(1, row) for b in range(w.B)])
         V = torch.cat([w.kv(b, int(L[b]), 1, device=DEV)[1].reshape(1, row) for b in range(w.B)])
         sd = t_dev(np.concatenate([w.slots(b, int(L[b]), 1) for b in range(w.B)]))
-        kv.kv_store_fp8(cache.handle, 0, K, V, row, row, sd, w.B)
+        kv.kv_store_fp8(h, 0, K, V, row, row, sd, w.B)
         q = w.q_decode(DEV)
-        got, ws_bytes = _decode_full(w, cache, q, w.total_lengths)
+        got, ws_bytes = _decode_full(w, _Handle(h), q, w.total_lengths, t_dev(tables))
         assert ws_bytes > 0                        # split-K with the reduce, as benchmarked
-        orc = OraclePools(w, cache.ks, cache.vs)
-        orc.store([(b, 0, int(w.total_lengths[b])) for b in range(w.B)])
-        orc.check_bytes(cache, "varlen")
-        want = orc.decode_all(bf16_bits(q), w.total_lengths)
+
+        # the oracle's pools: the blocks in use, renumbered 0.. in table order
+        ctables = np.zeros_like(tables)
+        used = []
+        pos = 0
+        for b in range(w.B):
+            ctables[b, :nblk[b]] = np.arange(pos, pos + nblk[b])
+            used.append(tables[b, :nblk[b]])
+            pos += nblk[b]
+        used = np.concatenate(used)
+        okp = np.zeros((pos, w.Hkv, w.BS * w.D), np.uint8)
+        ovp = np.zeros_like(okp)
+
+        def store(b):
+            Lb = int(w.total_lengths[b])
+            for lo in range(0, Lb, FILL_STEP):
+                n = min(FILL_STEP, Lb - lo)
+                k, v = w.kv(b, lo, n, device=DEV)
+                p_ = np.arange(lo, lo + n, dtype=np.int64)
+                slots = ctables[b, p_ // w.BS].astype(np.int64) * w.BS + p_ % w.BS
+                oracle.store(bf16_bits(k), bf16_bits(v), slots, okp, ovp, Hkv=w.Hkv, D=w.D, BS=w.BS,
+                             k_scale=np.float32(ks), v_scale=np.float32(vs))
+        _pmap(store, range(w.B))
+        bad_k = bad_v = 0
+        for lo in range(0, pos, 32768):
+            idx = torch.from_numpy(used[lo:lo + 32768].astype(np.int64)).to(DEV)
+            gk = k_pool.index_select(0, idx).cpu().numpy()
+            gv = v_pool.index_select(0, idx).cpu().numpy()
+            bad_k += int(np.count_nonzero(gk != okp[lo:lo + 32768]))
+            bad_v += int(np.count_nonzero(gv != ovp[lo:lo + 32768]))
+        assert bad_k == 0 and bad_v == 0, f"varlen: {bad_k} K and {bad_v} V bytes differ from the oracle"
+        lens = w.total_lengths.astype(np.int32)
+        qb = bf16_bits(q)
+
+        def one(b):
+            sel = np.array([[b, hh] for hh in range(w.Hq)], np.int32)
+            ref = oracle.decode_attn(qb, okp, ovp, ctables, lens, Hq=w.Hq, Hkv=w.Hkv, D=w.D, BS=w.BS,
+                                     k_scale=np.float32(ks), v_scale=np.float32(vs), sm_scale=w.sm_scale(), sel=sel)
+            return ref[b]
+        want = np.stack(_pmap(one, range(w.B)))
         assert_both(got, want, "varlen decode, every head")
     finally:
-        cache.close()
+        kv.kv_cache_free(h)
+        del k_pool, v_pool
+        torch.cuda.empty_cache()
 
 
 def test_longctx_full_size_with_shift():

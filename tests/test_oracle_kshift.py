@@ -79,6 +79,24 @@ def test_rope_table_pins(orc):
         assert abs(ang[-1] - delta * 1e6 ** (-254 / 256)) < 1e-6 * max(1, abs(delta))
 
 
+@pytest.mark.parametrize("rot", [256, 128, 96, 64, 2])
+@pytest.mark.parametrize("theta", [1e4, 1e6])
+@pytest.mark.parametrize("delta", [-4096, -1, 3, 7, 100000])
+def test_rope_table_every_pair(orc, rot, theta, delta):
+    """Every pair i of the table, for rotary widths equal to and below the head
+    dim: cos and sin of delta * theta^(-2i/rot), taken here by another route
+    (exp of a logarithm, numpy's fp64 cos/sin) and rounded to fp32, are the
+    table's values to within half an fp32 step (the two fp64 angles differ by a
+    few units of their last place).  An exponent over the head dim instead of
+    rot, over rot - 2, or a pair index off by one fails this at every rot."""
+    c, s = orc.rope_table(rot, delta, theta)
+    i = np.arange(rot // 2, dtype=np.float64)
+    ang = delta * np.exp(-2.0 * i / rot * np.log(np.float64(np.float32(theta))))
+    for got, ref in ((c, np.cos(ang)), (s, np.sin(ang))):
+        half_ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64) / 2
+        assert np.all(np.abs(got.astype(np.float64) - ref) <= half_ulp + 1e-11), (rot, theta, delta)
+
+
 def test_kshift_delta_zero_and_untouched_dims(orc):
     rng = np.random.default_rng(3)
     BS, Hkv, D = 16, 2, 128
