@@ -1,8 +1,10 @@
 """GPU parity of kv_store_fp8: cache bytes must equal the CPU oracle's bit for bit.
 
 Covers every bf16 bit pattern at several scales (including a negative scale,
-a tiny scale that lifts fp32 subnormals into range, and saturation), both
-the four-token-group and the single-token V write paths, negative slots,
+a tiny scale that lifts fp32 subnormals into range, and saturation) through
+the 16-token run path (consecutive slots) and the token-by-token path
+(shuffled slots), runs and broken runs in one call, both the four-token-group
+and the single-token V write paths, negative slots,
 padded token strides, untouched bytes, library-owned pools, and the store
 shapes of each workload at reduced size.
 """
@@ -87,6 +89,46 @@ def test_store_negative_slots_padding_and_untouched_bytes(BS, Hkv, D):
     ok, ov = _oracle_store(k, v, slots, NB, Hkv, D, BS, ks, vs, base, base)
     assert np.array_equal(gk, ok)
     assert np.array_equal(gv, ov)
+
+
+@pytest.mark.parametrize("BS,Hkv,D", [(16, 8, 128), (32, 3, 256), (16, 1, 64), (32, 2, 128), (16, 3, 64)])
+def test_store_sixteen_token_runs_and_broken_runs(BS, Hkv, D):
+    """One call whose 16-token groups take both write paths: whole runs of 16
+    consecutive slots from a multiple of 16 (block starts and the second half
+    of a 32-token block) are written tile by tile; groups whose run is broken
+    (a slot past the pool, a negative slot, a run starting 4 slots off, two
+    slots exchanged, a last group of 9 tokens) go token by token.  Every byte
+    must equal the oracle's, and untouched bytes keep their fill."""
+    rng = np.random.default_rng(BS + Hkv + D)
+    NB = 16
+    Hs = NB * BS
+    starts = [0, 16, BS * 5, BS * 7 + (16 if BS == 32 else 0)]
+    groups = [np.arange(st, st + 16) for st in starts]
+    g = np.arange(BS * 2, BS * 2 + 16)
+    g[7] = Hs + 3                                   # past the pool: skipped
+    groups.append(g)
+    g = np.arange(BS * 3, BS * 3 + 16)
+    g[0] = -1                                       # negative: skipped
+    groups.append(g)
+    groups.append(np.arange(BS * 12 + 4, BS * 12 + 20))  # consecutive, not 16-aligned
+    g = np.arange(BS * 10, BS * 10 + 16)
+    g[[3, 4]] = g[[4, 3]]                           # two slots exchanged
+    groups.append(g)
+    groups.append(np.arange(BS * 14, BS * 14 + 9))  # a last group of 9 tokens
+    slots = np.concatenate(groups).astype(np.int64)
+    valid = slots[(slots >= 0) & (slots < Hs)]
+    assert len(set(valid.tolist())) == valid.size
+    T = slots.size
+    k = rng.integers(0, 1 << 16, size=(T, Hkv, D), dtype=np.uint16)
+    v = rng.integers(0, 1 << 16, size=(T, Hkv, D), dtype=np.uint16)
+    log(f"store runs and broken runs: BS={BS} Hkv={Hkv} D={D} T={T}")
+    with GpuCache(NB, BS, Hkv, D, 0.031, -0.007, fill=0x5A) as c:
+        ks, vs = kv.kv_cache_get_scales(c.handle, 0)
+        gk, gv = _gpu_store(c, k, v, slots)
+    base = np.full((NB, Hkv, BS * D), 0x5A, np.uint8)
+    ok, ov = _oracle_store(k, v, slots, NB, Hkv, D, BS, ks, vs, base, base)
+    assert np.array_equal(gk, ok), f"K bytes differ at {np.count_nonzero(gk != ok)} positions"
+    assert np.array_equal(gv, ov), f"V bytes differ at {np.count_nonzero(gv != ov)} positions"
 
 
 def test_store_into_library_owned_pools():
