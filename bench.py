@@ -322,6 +322,28 @@ def _gather_ceiling(args, kv, w, handles, tables, max_blocks, lens, B, Hkv, kv_b
             "bytes": kv_bytes, "kernel": "gather_probe (one workgroup per (sequence, kv-head))"}
 
 
+def _kshift_ceiling(args, w, pools, slots, nsl, nbytes, stream):
+    """The K-shift's own traffic with no arithmetic (the rmw probe: the same
+    items and launch, each byte XORed with 1, in place) over the timed slot
+    list, and over the same slots in address order.  The first is the ceiling
+    of the K-shift through these block tables; the second shows what the
+    shuffled block order costs.  GB/s counts the K-shift's algorithmic bytes."""
+    import torch
+    import probe
+    ordered = torch.sort(slots).values
+    copies = len(pools)
+    out = {}
+    for name, sl in (("list_order", slots), ("address_order", ordered)):
+        def call(i, sl=sl):
+            probe.rmw(pools[i % copies][0], w.NB, w.Hkv, w.BS, w.D, w.D, sl, nsl, stream)
+        ms = _timed(call, args.steps, args.warmup, stream).mean()
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                     "ms_mean": round(ms, 5)}
+    out["kernel"] = "rmw_probe (the K-shift's items and grid-stride launch, XOR instead of the rotation)"
+    return out
+
+
 def _stream_ceiling(stream, nbytes=2 << 30, launches=20):
     """A plain streaming read (the read probe) of two alternating 2 GiB buffers:
     the achievable read bandwidth of this part, reported beside the 8 TB/s figure."""
@@ -815,6 +837,7 @@ def run_longctx(args):
     res["kv_shift_per_slot"] = dict(_stats(sp), algorithmic_bytes=sp_bytes, GBps=round(sp_gbps, 1),
                                     frac_hbm_peak=round(sp_gbps / HBM_PEAK_GBPS, 4), distinct_deltas=w.B,
                                     tokens_per_s=round(nsl / (sp.mean() * 1e-3), 1))
+    res["kv_shift_pattern_ceiling"] = _kshift_ceiling(args, w, pools, slots, nsl, sh_bytes, stream)
     dsha = _source_sha("decode.hip", "fp8_device.hpp", "decode_args.hpp")
     res["roofline"] = {"bound": "hbm", "achieved": round(de_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                        "frac": round(de_gbps / HBM_PEAK_GBPS, 4),

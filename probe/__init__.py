@@ -1,6 +1,7 @@
 """Measurement aids of the benchmark (not part of the kvfp8 library): a plain
-streaming read and a plain read of a paged decode's K/V tiles, built into
-probe/libkvf8probe.so from readprobe.hip (declared in readprobe.h)."""
+streaming read, a plain read of a paged decode's K/V tiles and the K-shift's
+in-place traffic with no arithmetic, built into probe/libkvf8probe.so from
+readprobe.hip (declared in readprobe.h)."""
 from __future__ import annotations
 
 import ctypes
@@ -48,6 +49,8 @@ def _load():
         lib.kvf8_probe_read.argtypes = [P, SZ, P, I32, P]
         lib.kvf8_probe_gather.restype = I32
         lib.kvf8_probe_gather.argtypes = [P, P, I64, I32, I32, I32, I32, I32, P, I32, P, I32, P, P]
+        lib.kvf8_probe_rmw.restype = I32
+        lib.kvf8_probe_rmw.argtypes = [P, I64, I32, I32, I32, I32, P, I64, P]
         _lib = lib
     return _lib
 
@@ -85,3 +88,9 @@ def gather(k_pool, v_pool, num_blocks: int, kv_heads: int, block_size: int, head
     _check(_load().kvf8_probe_gather(_ptr(k_pool), _ptr(v_pool), num_blocks, kv_heads, block_size, head_dim,
                                      k_elem_bytes, v_elem_bytes, _ptr(block_tables), max_blocks, _ptr(seq_lens),
                                      num_seqs, _ptr(out_words), _stream(stream)))
+
+
+def rmw(k_pool, num_blocks: int, kv_heads: int, block_size: int, head_dim: int, rot_dim: int, slots,
+        n_slots: int, stream=None) -> None:
+    _check(_load().kvf8_probe_rmw(_ptr(k_pool), num_blocks, kv_heads, block_size, head_dim, rot_dim,
+                                  _ptr(slots), n_slots, _stream(stream)))

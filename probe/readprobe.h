@@ -1,11 +1,13 @@
 /*
  * Measurement aids for the benchmark, not steps of the cache and not part of
  * the kvfp8 library: a plain streaming read of a device buffer (the part's
- * practical read-bandwidth ceiling) and a plain read of exactly the K/V tiles
- * a paged decode reads (the ceiling of its scattered access pattern).  Built
- * into libkvf8probe.so.  Every call checks its arguments on the host and
- * launches nothing when one is wrong; it returns 0 on success, 1 for an
- * invalid argument (message in kvf8_probe_last_error) and 6 for a HIP error.
+ * practical read-bandwidth ceiling), a plain read of exactly the K/V tiles a
+ * paged decode reads (the ceiling of its scattered access pattern) and the
+ * K-shift's in-place traffic with no arithmetic (the ceiling of its access
+ * pattern).  Built into libkvf8probe.so.  Every call checks its arguments on
+ * the host and launches nothing when one is wrong; it returns 0 on success, 1
+ * for an invalid argument (message in kvf8_probe_last_error) and 6 for a HIP
+ * error.
  */
 #ifndef KVF8_PROBE_H
 #define KVF8_PROBE_H
@@ -43,6 +45,23 @@ int kvf8_probe_gather(const void *k_pool, const void *v_pool, int64_t num_blocks
                       int32_t block_size, int32_t head_dim, int32_t k_elem_bytes, int32_t v_elem_bytes,
                       const int32_t *block_tables, int32_t max_blocks, const int32_t *seq_lens, int32_t num_seqs,
                       uint32_t *out_words, void *stream);
+
+/*
+ * The memory traffic of kv_shift_rope's run path (NEOX pairing) with no
+ * arithmetic: for every slot of `slots` (device, n_slots int64 entries;
+ * entries < 0 or >= num_blocks * block_size are skipped, as by the K-shift)
+ * and every kv-head, the bytes of dims [0, rot_dim/2) and their partners
+ * [rot_dim/2, rot_dim) of the slot's K row are read and written back XORed
+ * with 0x01, in place, 16 bytes per access, through the same work items and
+ * grid-stride launch as the K-shift.  Applying it twice restores the pool.
+ * k_pool (device): [num_blocks][num_kv_heads][block_size * head_dim] E4M3
+ * codes.  block_size in {16, 32}, head_dim in {64, 128, 256}, rot_dim a
+ * multiple of 32 in [32, head_dim].  n_slots == 0 is a no-op.  Calls that
+ * name the same slot twice, or overlap on one pool, race.  Asynchronous on
+ * `stream`.
+ */
+int kvf8_probe_rmw(void *k_pool, int64_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                   int32_t rot_dim, const int64_t *slots, int64_t n_slots, void *stream);
 
 #ifdef __cplusplus
 }

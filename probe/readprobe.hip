@@ -13,7 +13,14 @@
 // tiles through the block table (block ids staged in LDS, four 16-byte loads
 // in flight per lane, K tiles then V tiles) and writes their XOR.  Its rate
 // is the ceiling of the decode's access pattern (scattered tiles), as
-// opposed to a linear stream.  Measurement aids of the benchmark only, built
+// opposed to a linear stream.
+//
+// kvf8_probe_rmw: the K-shift's memory traffic with no arithmetic.  The same
+// work items as the run path of the NEOX K-shift (a (slot, head) item and a
+// 16-byte run r: dims [16r, 16r + 16) and their partners rot/2 further, both
+// read and written in place), the same grid-stride launch, but each byte is
+// only XORed with 1.  Its rate is the ceiling of the K-shift's access pattern
+// through a given slot list.  Measurement aids of the benchmark only, built
 // into their own library (libkvf8probe.so), not into the cache library.
 
 #include <hip/hip_runtime.h>
@@ -120,6 +127,56 @@ __global__ __launch_bounds__(kThreads) void gather_probe(GatherArgs a) {
     }
 }
 
+constexpr int64_t kRmwMaxWgs = 4096;     // as the K-shift's run path: 16 workgroups per CU, then a grid stride
+
+struct RmwArgs {
+    uint8_t *k_pool;
+    const int64_t *slots;
+    int64_t n_slots;
+    int64_t pool_slots;
+    int32_t kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t runs;            // 16-byte runs of the rotated first half: rot_dim / 32
+    int32_t half;            // rot_dim / 2: byte distance of a run's partner
+    int32_t rp_log2;         // runs rounded up to a power of two
+};
+
+__device__ __forceinline__ int64_t k_byte(int t, int d, int BS, int D) {
+    const int q = D >> 2;
+    return ((int64_t)(d / q) * BS + t) * q + d % q;
+}
+
+__global__ __launch_bounds__(kThreads) void rmw_probe(RmwArgs a) {
+    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int r = (int)(g & ((1 << a.rp_log2) - 1));
+    const int64_t nj = a.n_slots * a.kv_heads;
+    if (r >= a.runs) return;
+    const int bs_log2 = a.block_size == 32 ? 5 : 4;
+    const int64_t jstep = ((int64_t)gridDim.x * kThreads) >> a.rp_log2;
+    for (int64_t j = g >> a.rp_log2; j < nj; j += jstep) {
+        int64_t si;
+        int h;
+        if (nj <= 0x7FFFFFFF) {                 // 32-bit division, as the K-shift
+            si = (uint32_t)j / (uint32_t)a.kv_heads;
+            h = (int)((uint32_t)j - (uint32_t)si * (uint32_t)a.kv_heads);
+        } else {
+            si = j / a.kv_heads;
+            h = (int)(j - si * a.kv_heads);
+        }
+        const int64_t slot = a.slots[si];
+        if (slot < 0 || slot >= a.pool_slots) continue;
+        const int64_t blk = slot >> bs_log2;
+        const int t = (int)(slot - (blk << bs_log2));
+        uint8_t *tile = a.k_pool + ((blk * a.kv_heads + h) << bs_log2) * a.head_dim;
+        u32x4 *pa = reinterpret_cast<u32x4 *>(tile + k_byte(t, 16 * r, a.block_size, a.head_dim));
+        u32x4 *pb = reinterpret_cast<u32x4 *>(tile + k_byte(t, 16 * r + a.half, a.block_size, a.head_dim));
+        const u32x4 va = *pa, vb = *pb;
+        *pa = va ^ 0x01010101u;
+        *pb = vb ^ 0x01010101u;
+    }
+}
+
 thread_local std::string g_last_error;
 
 int fail(const char *fmt, ...) {
@@ -201,6 +258,37 @@ int kvf8_probe_gather(const void *k_pool, const void *v_pool, int64_t num_blocks
     hipLaunchKernelGGL(gather_probe, dim3((unsigned)(num_seqs * num_kv_heads)), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), a);
     return launched("kvf8_probe_gather launch");
+}
+
+int kvf8_probe_rmw(void *k_pool, int64_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                   int32_t rot_dim, const int64_t *slots, int64_t n_slots, void *stream) {
+    if (num_blocks <= 0 || num_kv_heads <= 0) return fail("num_blocks and num_kv_heads must be positive");
+    if ((block_size != 16 && block_size != 32) || (head_dim != 64 && head_dim != 128 && head_dim != 256))
+        return fail("block_size must be 16 or 32 and head_dim 64, 128 or 256");
+    if (rot_dim < 32 || rot_dim > head_dim || rot_dim % 32 != 0)
+        return fail("rot_dim must be a multiple of 32 in [32, head_dim]");
+    if (n_slots < 0) return fail("n_slots must be >= 0");
+    if (n_slots == 0) {
+        g_last_error.clear();
+        return 0;
+    }
+    if (!k_pool || !slots) return fail("k_pool and slots must be non-NULL");
+    if (n_slots > (int64_t(1) << 40) / num_kv_heads) return fail("too many slots");
+    RmwArgs a{};
+    a.k_pool = static_cast<uint8_t *>(k_pool);
+    a.slots = slots;
+    a.n_slots = n_slots;
+    a.pool_slots = num_blocks * block_size;
+    a.kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.runs = rot_dim / 32;
+    a.half = rot_dim / 2;
+    while ((1 << a.rp_log2) < a.runs) ++a.rp_log2;
+    int64_t wgs = (((n_slots * num_kv_heads) << a.rp_log2) + kThreads - 1) / kThreads;
+    if (wgs > kRmwMaxWgs) wgs = kRmwMaxWgs;
+    hipLaunchKernelGGL(rmw_probe, dim3((unsigned)wgs), dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
+    return launched("kvf8_probe_rmw launch");
 }
 
 }  // extern "C"

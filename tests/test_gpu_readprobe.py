@@ -1,7 +1,9 @@
-"""GPU check of the streaming-read measurement aid: the XOR of the per-workgroup
-words must equal the XOR of every 32-bit word of the buffer (so every byte was
-read), for several sizes and worker counts, including a buffer smaller than one
-grid pass and one that is not a multiple of the unrolled stride."""
+"""GPU checks of the measurement aids: the streaming read's per-workgroup XOR
+words must XOR to the XOR of every 32-bit word of the buffer (so every byte
+was read), for several sizes and worker counts, including a buffer smaller
+than one grid pass and one that is not a multiple of the unrolled stride; the
+paged-gather read covers exactly a decode's tiles; the K-shift traffic probe
+touches exactly the K-shift's bytes."""
 import numpy as np
 import pytest
 import torch
@@ -58,3 +60,34 @@ def test_gather_probe_xor(BS, Hkv, D, v_elem):
             if blocks.size:
                 want = np.bitwise_xor.reduce(np.concatenate([kt[blocks, hh].ravel(), vt[blocks, hh].ravel()]))
             assert int(got[b * Hkv + hh]) == int(want), (b, hh)
+
+
+@pytest.mark.parametrize("BS,Hkv,D,rot", [(16, 2, 64, 64), (32, 2, 256, 256), (16, 3, 128, 64), (16, 1, 64, 32)])
+def test_rmw_probe_touches_the_kshift_bytes(BS, Hkv, D, rot):
+    """One pass flips bit 0 of exactly the rotated bytes (dims [0, rot)) of the
+    listed in-pool slots in every kv-head and nothing else; a second pass
+    restores the pool."""
+    rng = np.random.default_rng(BS + Hkv + D + rot)
+    NB = 9
+    pool = rng.integers(0, 256, size=(NB, Hkv, BS * D), dtype=np.uint8)
+    slots = rng.choice(NB * BS, size=NB * BS // 2, replace=False).astype(np.int64)
+    slots = np.concatenate([slots, [-1, NB * BS, NB * BS + 5]])
+    rng.shuffle(slots)
+    log(f"rmw probe BS={BS} Hkv={Hkv} D={D} rot={rot}")
+    dev = torch.from_numpy(pool).to(DEV)
+    sd = torch.from_numpy(slots).to(DEV)
+    probe.rmw(dev, NB, Hkv, BS, D, rot, sd, slots.size)
+    torch.cuda.synchronize()
+    once = dev.cpu().numpy()
+    want = pool.copy()
+    q = D // 4
+    for s in slots:
+        if s < 0 or s >= NB * BS:
+            continue
+        b, t = divmod(int(s), BS)
+        for d in range(rot):
+            want[b, :, (d // q) * BS * q + t * q + d % q] ^= 1
+    assert np.array_equal(once, want)
+    probe.rmw(dev, NB, Hkv, BS, D, rot, sd, slots.size)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev.cpu().numpy(), pool)

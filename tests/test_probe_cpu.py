@@ -36,3 +36,18 @@ def test_gather_probe_host_checks():
             probe.gather(a["k"], a["v"], a["nb"], a["h"], a["bs"], a["d"], a["keb"], a["veb"], a["t"], a["mb"],
                          a["l"], a["n"], a["o"], 0)
         assert ei.value.status == E_INVALID, change
+
+
+def test_rmw_probe_host_checks():
+    """The K-shift traffic probe refuses bad shapes, rotary widths off the run
+    path, negative counts and NULL pointers; no slots is a no-op."""
+    K, S = 1 << 33, 1 << 34
+    good = dict(k=K, nb=8, h=2, bs=16, d=64, rot=64, s=S, n=5)
+    probe.rmw(None, 8, 2, 16, 64, 64, None, 0, 0)
+    bad = [dict(nb=0), dict(h=0), dict(bs=8), dict(d=96), dict(rot=16), dict(rot=48), dict(rot=128), dict(n=-1),
+           dict(k=None), dict(s=None)]
+    for change in bad:
+        a = {**good, **change}
+        with pytest.raises(probe.ProbeError) as ei:
+            probe.rmw(a["k"], a["nb"], a["h"], a["bs"], a["d"], a["rot"], a["s"], a["n"], 0)
+        assert ei.value.status == E_INVALID, change
