@@ -214,6 +214,11 @@ def run_llama8b(args):
                                                      w.Hkv, kv_bytes, stream)
     result["decode"]["frac_of_gather_ceiling"] = round(
         decode_gbps / result["paged_gather_ceiling"]["GBps"], 4)
+    # the fill's own traffic with no arithmetic (overwrites the pools: after every read of them)
+    result["kv_store"]["pattern_ceiling"] = _store_ceiling(args, w, pools, K, V, row, slots_d, T, store_bytes,
+                                                           stream)
+    result["kv_store"]["frac_of_pattern_ceiling"] = round(
+        store_gbps / result["kv_store"]["pattern_ceiling"]["list_order"]["GBps"], 4)
     result["calibrate"] = _calibrate(args, kv, K, V, T, row, ks, vs, stream)
     for h in handles:
         kv.kv_cache_free(h)
@@ -341,6 +346,30 @@ def _kshift_ceiling(args, w, pools, slots, nsl, nbytes, stream):
         out[name] = {"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                      "ms_mean": round(ms, 5)}
     out["kernel"] = "rmw_probe (the K-shift's items and grid-stride launch, XOR instead of the rotation)"
+    return out
+
+
+def _store_ceiling(args, w, pools, K, V, row, slots, T, nbytes, stream):
+    """The cache fill's own traffic with no arithmetic (the store_copy probe:
+    the store's 16-token run path, each value's high byte written where the
+    store writes its code) over the same inputs and rotating pools: with the
+    timed slot list, the ceiling of the fill's access pattern; with token i
+    going to slot i, what the shuffled block order costs.  GB/s counts the
+    store's algorithmic bytes."""
+    import torch
+    import probe
+    copies = len(pools)
+    out = {}
+    # the timed slot list, and token i to slot i (blocks handed out in address order)
+    for name, sl in (("list_order", slots), ("address_order", torch.arange(T, dtype=torch.int64, device="cuda"))):
+        def call(i, sl=sl):
+            kp, vp = pools[i % copies]
+            probe.store_copy(K, V, row, row, sl, T, kp, vp, w.NB, w.Hkv, w.BS, w.D, stream)
+
+        ms = _timed(call, args.steps, args.warmup, stream).mean()
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "ms_mean": round(ms, 5)}
+    out["kernel"] = "store_copy_probe (the store's run path, high bytes instead of codes)"
     return out
 
 

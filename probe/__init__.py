@@ -1,7 +1,7 @@
 """Measurement aids of the benchmark (not part of the kvfp8 library): a plain
-streaming read, a plain read of a paged decode's K/V tiles and the K-shift's
-in-place traffic with no arithmetic, built into probe/libkvf8probe.so from
-readprobe.hip (declared in readprobe.h)."""
+streaming read, a plain read of a paged decode's K/V tiles, and the K-shift's
+and the cache fill's traffic with no arithmetic, built into
+probe/libkvf8probe.so from readprobe.hip (declared in readprobe.h)."""
 from __future__ import annotations
 
 import ctypes
@@ -51,6 +51,8 @@ def _load():
         lib.kvf8_probe_gather.argtypes = [P, P, I64, I32, I32, I32, I32, I32, P, I32, P, I32, P, P]
         lib.kvf8_probe_rmw.restype = I32
         lib.kvf8_probe_rmw.argtypes = [P, I64, I32, I32, I32, I32, P, I64, P]
+        lib.kvf8_probe_store_copy.restype = I32
+        lib.kvf8_probe_store_copy.argtypes = [P, P, I64, I64, P, I64, P, P, I64, I32, I32, I32, P]
         _lib = lib
     return _lib
 
@@ -94,3 +96,10 @@ def rmw(k_pool, num_blocks: int, kv_heads: int, block_size: int, head_dim: int, 
         n_slots: int, stream=None) -> None:
     _check(_load().kvf8_probe_rmw(_ptr(k_pool), num_blocks, kv_heads, block_size, head_dim, rot_dim,
                                   _ptr(slots), n_slots, _stream(stream)))
+
+
+def store_copy(k, v, k_stride: int, v_stride: int, slots, num_tokens: int, k_pool, v_pool, num_blocks: int,
+               kv_heads: int, block_size: int, head_dim: int, stream=None) -> None:
+    _check(_load().kvf8_probe_store_copy(_ptr(k), _ptr(v), k_stride, v_stride, _ptr(slots), num_tokens,
+                                         _ptr(k_pool), _ptr(v_pool), num_blocks, kv_heads, block_size, head_dim,
+                                         _stream(stream)))

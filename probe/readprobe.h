@@ -2,9 +2,9 @@
  * Measurement aids for the benchmark, not steps of the cache and not part of
  * the kvfp8 library: a plain streaming read of a device buffer (the part's
  * practical read-bandwidth ceiling), a plain read of exactly the K/V tiles a
- * paged decode reads (the ceiling of its scattered access pattern) and the
- * K-shift's in-place traffic with no arithmetic (the ceiling of its access
- * pattern).  Built into libkvf8probe.so.  Every call checks its arguments on
+ * paged decode reads (the ceiling of its scattered access pattern), and the
+ * K-shift's and the cache fill's traffic with no arithmetic (the ceilings of
+ * their access patterns).  Built into libkvf8probe.so.  Every call checks its arguments on
  * the host and launches nothing when one is wrong; it returns 0 on success, 1
  * for an invalid argument (message in kvf8_probe_last_error) and 6 for a HIP
  * error.
@@ -62,6 +62,25 @@ int kvf8_probe_gather(const void *k_pool, const void *v_pool, int64_t num_blocks
  */
 int kvf8_probe_rmw(void *k_pool, int64_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
                    int32_t rot_dim, const int64_t *slots, int64_t n_slots, void *stream);
+
+/*
+ * The memory traffic of kv_store_fp8's 16-token run path with no arithmetic:
+ * every group of 16 consecutive input tokens (token 16i .. 16i + 15) whose
+ * slots are 16 consecutive slots s0 .. s0 + 15 with s0 a multiple of 16,
+ * inside the pool (num_blocks * block_size slots), is read and written with
+ * the store's workgroups, pieces and loads, but the byte written where the
+ * store writes a value's code is the high byte of the value's bf16 bits.
+ * Other groups (and a last partial one) are left alone.  k / v (device):
+ * [num_tokens][*_stride] bf16 bits, rows of num_kv_heads * head_dim values,
+ * strides multiples of 8 elements and >= that row; slots (device):
+ * num_tokens int64; k_pool / v_pool (device): [num_blocks][num_kv_heads]
+ * [block_size * head_dim] bytes in the cache's E4M3 layout.  k, v and the
+ * pools 16-byte aligned; block_size in {16, 32}, head_dim in {64, 128, 256}.
+ * num_tokens == 0 is a no-op.  Asynchronous on `stream`.
+ */
+int kvf8_probe_store_copy(const uint16_t *k, const uint16_t *v, int64_t k_stride, int64_t v_stride,
+                          const int64_t *slots, int64_t num_tokens, void *k_pool, void *v_pool, int64_t num_blocks,
+                          int32_t num_kv_heads, int32_t block_size, int32_t head_dim, void *stream);
 
 #ifdef __cplusplus
 }

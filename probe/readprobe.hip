@@ -20,8 +20,16 @@
 // 16-byte run r: dims [16r, 16r + 16) and their partners rot/2 further, both
 // read and written in place), the same grid-stride launch, but each byte is
 // only XORed with 1.  Its rate is the ceiling of the K-shift's access pattern
-// through a given slot list.  Measurement aids of the benchmark only, built
-// into their own library (libkvf8probe.so), not into the cache library.
+// through a given slot list.
+//
+// kvf8_probe_store_copy: the cache fill's memory traffic with no arithmetic.
+// The same workgroups, pieces and loads as the store's 16-token run path
+// (one workgroup per 16 input tokens bound for one aligned run of 16 slots;
+// K pieces of 16 dims of a token, V pieces of 8 dims x 4 tokens), but each
+// bf16 value's high byte is written where the store writes its code.  Its
+// rate is the ceiling of the fill's access pattern through a given slot list.
+// Measurement aids of the benchmark only, built into their own library
+// (libkvf8probe.so), not into the cache library.
 
 #include <hip/hip_runtime.h>
 
@@ -177,6 +185,122 @@ __global__ __launch_bounds__(kThreads) void rmw_probe(RmwArgs a) {
     }
 }
 
+struct CopyArgs {
+    const uint16_t *k;
+    const uint16_t *v;
+    int64_t k_stride;        // elements between consecutive tokens' rows
+    int64_t v_stride;
+    const int64_t *slots;
+    int64_t num_tokens;
+    int64_t pool_slots;
+    uint8_t *k_pool;
+    uint8_t *v_pool;
+    int32_t kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+};
+
+// High bytes of four bf16 values (two words): bytes 1, 3 of p0, then of p1.
+__device__ __forceinline__ uint32_t hi_bytes(uint32_t p0, uint32_t p1) {
+    return __builtin_amdgcn_perm(p1, p0, 0x07050301u);
+}
+
+__global__ __launch_bounds__(kThreads) void store_copy_probe(CopyArgs a) {
+    const int64_t tok0 = (int64_t)blockIdx.x * 16;
+    __shared__ int64_t s_first;
+    __shared__ int s_run;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        int64_t s = -1;
+        if (lane < 16 && tok0 + lane < a.num_tokens) s = a.slots[tok0 + lane];
+        const int64_t s0 = __shfl(s, 0);
+        const bool ok = lane >= 16 || (s == s0 + lane && s >= 0 && s < a.pool_slots);
+        const bool run = __all(ok) && (s0 & 15) == 0;
+        if (lane == 0) {
+            s_first = s0;
+            s_run = run ? 1 : 0;
+        }
+    }
+    __syncthreads();
+    if (!s_run) return;                          // only whole aligned 16-token runs are copied
+    const int D = a.head_dim, H = a.kv_heads, BS = a.block_size;
+    const int Q4 = D >> 2;
+    const int64_t tile = (int64_t)BS * D;
+    const int64_t blk = s_first / BS;
+    const int t0 = (int)(s_first - blk * BS);
+    const int np = D >> 6;
+    const int kper = 16 * (D >> 4);
+    const int vper = 4 * (D >> 3);
+    const int k_items = H * kper, v_items = H * vper;
+    for (int base = 0; base < k_items; base += 4 * kThreads) {
+        u32x4 lo[4], hi[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int it = base + u * kThreads + threadIdx.x;
+            if (it < k_items) {
+                const int h = it / kper;
+                const int r = it - h * kper;
+                const int j = r % np, t = (r / np) & 15, q = r / (16 * np);
+                const u32x4 *src =
+                    reinterpret_cast<const u32x4 *>(a.k + (tok0 + t) * a.k_stride + (int64_t)h * D + q * Q4 + j * 16);
+                lo[u] = src[0];
+                hi[u] = src[1];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int it = base + u * kThreads + threadIdx.x;
+            if (it < k_items) {
+                const int h = it / kper;
+                const int r = it - h * kper;
+                const int j = r % np, t = (r / np) & 15, q = r / (16 * np);
+                const int64_t off = (blk * H + h) * tile + (int64_t)(q * BS + t0 + t) * Q4 + j * 16;
+                const u32x4 c = {hi_bytes(lo[u][0], lo[u][1]), hi_bytes(lo[u][2], lo[u][3]),
+                                 hi_bytes(hi[u][0], hi[u][1]), hi_bytes(hi[u][2], hi[u][3])};
+                *reinterpret_cast<u32x4 *>(a.k_pool + off) = c;
+            }
+        }
+    }
+    for (int base = 0; base < v_items; base += 2 * kThreads) {
+        u32x4 x[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int it = base + u * kThreads + threadIdx.x;
+            if (it < v_items) {
+                const int h = it / vper;
+                const int r = it - h * vper;
+                const int g = r / (D >> 3), o = r - g * (D >> 3);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    x[u][k] = *reinterpret_cast<const u32x4 *>(a.v + (tok0 + 4 * g + k) * a.v_stride + (int64_t)h * D +
+                                                               8 * o);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int it = base + u * kThreads + threadIdx.x;
+            if (it < v_items) {
+                const int h = it / vper;
+                const int r = it - h * vper;
+                const int g = r / (D >> 3), o = r - g * (D >> 3);
+                u32x4 out[2];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {           // dim 8o + j: four tokens' high bytes
+                    const int w = j >> 1;
+                    const uint32_t sel = (j & 1) ? 0x07030703u : 0x05010501u;
+                    const uint32_t lo = __builtin_amdgcn_perm(x[u][1][w], x[u][0][w], sel);
+                    const uint32_t hi = __builtin_amdgcn_perm(x[u][3][w], x[u][2][w], sel);
+                    out[j >> 2][j & 3] = (lo & 0xFFFFu) | (hi << 16);
+                }
+                u32x4 *dst = reinterpret_cast<u32x4 *>(a.v_pool + (blk * H + h) * tile +
+                                                       ((int64_t)(t0 / 4 + g) * D + 8 * o) * 4);
+                dst[0] = out[0];
+                dst[1] = out[1];
+            }
+        }
+    }
+}
+
 thread_local std::string g_last_error;
 
 int fail(const char *fmt, ...) {
@@ -289,6 +413,43 @@ int kvf8_probe_rmw(void *k_pool, int64_t num_blocks, int32_t num_kv_heads, int32
     if (wgs > kRmwMaxWgs) wgs = kRmwMaxWgs;
     hipLaunchKernelGGL(rmw_probe, dim3((unsigned)wgs), dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
     return launched("kvf8_probe_rmw launch");
+}
+
+int kvf8_probe_store_copy(const uint16_t *k, const uint16_t *v, int64_t k_stride, int64_t v_stride,
+                          const int64_t *slots, int64_t num_tokens, void *k_pool, void *v_pool, int64_t num_blocks,
+                          int32_t num_kv_heads, int32_t block_size, int32_t head_dim, void *stream) {
+    if (num_blocks <= 0 || num_kv_heads <= 0) return fail("num_blocks and num_kv_heads must be positive");
+    if ((block_size != 16 && block_size != 32) || (head_dim != 64 && head_dim != 128 && head_dim != 256))
+        return fail("block_size must be 16 or 32 and head_dim 64, 128 or 256");
+    if (num_tokens < 0) return fail("num_tokens must be >= 0");
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if (k_stride < row || v_stride < row) return fail("token strides must be >= num_kv_heads * head_dim");
+    if (k_stride % 8 != 0 || v_stride % 8 != 0) return fail("token strides must be multiples of 8 elements");
+    if (num_tokens == 0) {
+        g_last_error.clear();
+        return 0;
+    }
+    if (!k || !v || !slots || !k_pool || !v_pool) return fail("k, v, slots and pools must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(k_pool) |
+         reinterpret_cast<uintptr_t>(v_pool)) % 16 != 0)
+        return fail("k, v and the pools must be 16-byte aligned");
+    const int64_t wgs = (num_tokens + 15) / 16;
+    if (wgs > 0x7FFFFFFF) return fail("too many tokens");
+    CopyArgs a{};
+    a.k = k;
+    a.v = v;
+    a.k_stride = k_stride;
+    a.v_stride = v_stride;
+    a.slots = slots;
+    a.num_tokens = num_tokens;
+    a.pool_slots = num_blocks * block_size;
+    a.k_pool = static_cast<uint8_t *>(k_pool);
+    a.v_pool = static_cast<uint8_t *>(v_pool);
+    a.kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    hipLaunchKernelGGL(store_copy_probe, dim3((unsigned)wgs), dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
+    return launched("kvf8_probe_store_copy launch");
 }
 
 }  // extern "C"

@@ -3,7 +3,8 @@ words must XOR to the XOR of every 32-bit word of the buffer (so every byte
 was read), for several sizes and worker counts, including a buffer smaller
 than one grid pass and one that is not a multiple of the unrolled stride; the
 paged-gather read covers exactly a decode's tiles; the K-shift traffic probe
-touches exactly the K-shift's bytes."""
+touches exactly the K-shift's bytes, and the fill traffic probe writes exactly
+where the store writes, for whole aligned 16-token runs only."""
 import numpy as np
 import pytest
 import torch
@@ -91,3 +92,41 @@ def test_rmw_probe_touches_the_kshift_bytes(BS, Hkv, D, rot):
     probe.rmw(dev, NB, Hkv, BS, D, rot, sd, slots.size)
     torch.cuda.synchronize()
     assert np.array_equal(dev.cpu().numpy(), pool)
+
+
+@pytest.mark.parametrize("BS,Hkv,D", [(16, 2, 64), (32, 3, 128), (16, 1, 256)])
+def test_store_copy_probe_writes_the_store_positions(BS, Hkv, D):
+    """Groups of 16 tokens bound for an aligned run of 16 slots get each bf16
+    value's high byte at the byte the store's layout gives that (token, dim);
+    a group whose run is broken, one whose run is not aligned, one past the
+    pool and a short last group leave the pools untouched."""
+    rng = np.random.default_rng(BS + Hkv + D)
+    NB = 8
+    row = Hkv * D
+    stride = row + 8
+    runs = [np.arange(16 * i, 16 * i + 16) for i in (3, 0, 5)]                   # whole aligned runs
+    broken = np.arange(16 * 6, 16 * 6 + 16)[::-1]                               # reversed
+    shifted = np.arange(16 * 1 + 8, 16 * 1 + 24)                                # not aligned
+    past = np.arange(NB * BS, NB * BS + 16)                                     # outside the pool
+    short = np.arange(16 * 7, 16 * 7 + 5)                                       # last, partial
+    slots = np.concatenate(runs + [broken, shifted, past, short]).astype(np.int64)
+    n = slots.size
+    kb = rng.integers(0, 1 << 16, size=(n, stride), dtype=np.uint16)
+    vb = rng.integers(0, 1 << 16, size=(n, stride), dtype=np.uint16)
+    log(f"store copy probe BS={BS} Hkv={Hkv} D={D}")
+    kp = torch.zeros((NB, Hkv, BS * D), dtype=torch.uint8, device=DEV)
+    vp = torch.zeros_like(kp)
+    probe.store_copy(torch.from_numpy(kb.view(np.int16)).to(DEV), torch.from_numpy(vb.view(np.int16)).to(DEV),
+                     stride, stride, torch.from_numpy(slots).to(DEV), n, kp, vp, NB, Hkv, BS, D)
+    torch.cuda.synchronize()
+    want_k = np.zeros((NB, Hkv, BS * D), np.uint8)
+    want_v = np.zeros_like(want_k)
+    q = D // 4
+    d = np.arange(D)
+    for i in range(3 * 16):
+        b, t = divmod(int(slots[i]), BS)
+        for h in range(Hkv):
+            want_k[b, h, ((d // q) * BS + t) * q + d % q] = (kb[i, h * D + d] >> 8).astype(np.uint8)
+            want_v[b, h, ((t // 4) * D + d) * 4 + t % 4] = (vb[i, h * D + d] >> 8).astype(np.uint8)
+    assert np.array_equal(kp.cpu().numpy(), want_k)
+    assert np.array_equal(vp.cpu().numpy(), want_v)

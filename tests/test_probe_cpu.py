@@ -51,3 +51,19 @@ def test_rmw_probe_host_checks():
         with pytest.raises(probe.ProbeError) as ei:
             probe.rmw(a["k"], a["nb"], a["h"], a["bs"], a["d"], a["rot"], a["s"], a["n"], 0)
         assert ei.value.status == E_INVALID, change
+
+
+def test_store_copy_probe_host_checks():
+    """The fill traffic probe refuses bad shapes, short or ragged strides,
+    misaligned buffers and NULL pointers; no tokens is a no-op."""
+    K, V, S, KP, VP = 1 << 33, 1 << 34, 1 << 35, 1 << 36, 1 << 37
+    good = dict(k=K, v=V, ks=256, vs=256, s=S, n=32, kp=KP, vp=VP, nb=8, h=2, bs=16, d=128)
+    probe.store_copy(None, None, 256, 256, None, 0, None, None, 8, 2, 16, 128, 0)
+    bad = [dict(nb=0), dict(h=0), dict(bs=8), dict(d=96), dict(n=-1), dict(ks=128), dict(vs=260),
+           dict(k=None), dict(v=None), dict(s=None), dict(kp=None), dict(vp=None), dict(k=K + 8), dict(vp=VP + 4)]
+    for change in bad:
+        a = {**good, **change}
+        with pytest.raises(probe.ProbeError) as ei:
+            probe.store_copy(a["k"], a["v"], a["ks"], a["vs"], a["s"], a["n"], a["kp"], a["vp"], a["nb"], a["h"],
+                             a["bs"], a["d"], 0)
+        assert ei.value.status == E_INVALID, change
