@@ -307,24 +307,33 @@ def _typed_exchange(args, kv, w, K, V, slots_d, T, q, tables, lens, max_len, out
     return res
 
 
-def _gather_ceiling(args, kv, w, handles, tables, max_blocks, lens, B, Hkv, kv_bytes, stream):
+def _gather_ceiling(args, kv, w, handles, tables, max_blocks, lens, B, Hkv, kv_bytes, stream, chunk_blocks=None):
     """The gather probe over the decode's own pools and block tables: a plain
     read of exactly the K/V tiles the decode reads, the ceiling of its
-    scattered-tile access pattern.  GB/s counts the K/V bytes only."""
+    scattered-tile access pattern; one workgroup per (sequence, kv-head), or
+    per chunk of chunk_blocks table entries of one.  GB/s counts the K/V
+    bytes only."""
     import torch
     import probe
-    out = torch.empty(B * Hkv, dtype=torch.int32, device="cuda")
+    chunks = 1 if chunk_blocks is None else -(-max_blocks // chunk_blocks)
+    out = torch.empty(chunks * B * Hkv, dtype=torch.int32, device="cuda")
     pools = [kv.kv_cache_pools(h, 0) for h in handles]
     copies = len(handles)
 
     def call(i):
         kp, vp, _ = pools[(i + 1) % copies]
-        probe.gather(kp, vp, w.NB, w.Hkv, w.BS, w.D, 1, 1, tables, max_blocks, lens, B, out, stream)
+        if chunk_blocks is None:
+            probe.gather(kp, vp, w.NB, w.Hkv, w.BS, w.D, 1, 1, tables, max_blocks, lens, B, out, stream)
+        else:
+            probe.gather_split(kp, vp, w.NB, w.Hkv, w.BS, w.D, 1, 1, tables, max_blocks, lens, B, chunk_blocks, out,
+                               stream)
 
     ms = _timed(call, args.steps, args.warmup, stream).mean()
     gbps = kv_bytes / (ms * 1e-3) / 1e9
+    what = ("one workgroup per (sequence, kv-head)" if chunk_blocks is None else
+            f"one workgroup per {chunk_blocks} blocks of one (sequence, kv-head)")
     return {"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "ms_mean": round(ms, 5),
-            "bytes": kv_bytes, "kernel": "gather_probe (one workgroup per (sequence, kv-head))"}
+            "bytes": kv_bytes, "kernel": f"gather_probe ({what})"}
 
 
 def _kshift_ceiling(args, w, pools, slots, nsl, nbytes, stream):
@@ -867,6 +876,11 @@ def run_longctx(args):
                                     frac_hbm_peak=round(sp_gbps / HBM_PEAK_GBPS, 4), distinct_deltas=w.B,
                                     tokens_per_s=round(nsl / (sp.mean() * 1e-3), 1))
     res["kv_shift_pattern_ceiling"] = _kshift_ceiling(args, w, pools, slots, nsl, sh_bytes, stream)
+    # the decode's tiles read with no compute, split into the decode's own chunks
+    kv_bytes = int(np.sum(lens)) * 2 * w.Hkv * w.D
+    res["paged_gather_ceiling"] = _gather_ceiling(args, kv, w, handles, tables, w.max_blocks, lens_d, w.B, w.Hkv,
+                                                  kv_bytes, stream, chunk_blocks=4096 // w.BS)
+    res["decode"]["frac_of_gather_ceiling"] = round(de_gbps / res["paged_gather_ceiling"]["GBps"], 4)
     dsha = _source_sha("decode.hip", "fp8_device.hpp", "decode_args.hpp")
     res["roofline"] = {"bound": "hbm", "achieved": round(de_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                        "frac": round(de_gbps / HBM_PEAK_GBPS, 4),
@@ -967,6 +981,10 @@ def run_varlen(args):
     res["paged_gather_unsplit"] = _gather_ceiling(args, kv, w, [h], tables, w.max_blocks, lens_d, w.B, w.Hkv,
                                                   kv_bytes, stream)
     res["decode"]["speedup_over_unsplit_gather"] = round(de_gbps / res["paged_gather_unsplit"]["GBps"], 4)
+    # and split into the decode's own 4096-token chunks
+    res["paged_gather_ceiling"] = _gather_ceiling(args, kv, w, [h], tables, w.max_blocks, lens_d, w.B, w.Hkv,
+                                                  kv_bytes, stream, chunk_blocks=4096 // w.BS)
+    res["decode"]["frac_of_gather_ceiling"] = round(de_gbps / res["paged_gather_ceiling"]["GBps"], 4)
     kv.kv_cache_free(h)
     del kp, vp
     torch.cuda.empty_cache()

@@ -49,6 +49,8 @@ def _load():
         lib.kvf8_probe_read.argtypes = [P, SZ, P, I32, P]
         lib.kvf8_probe_gather.restype = I32
         lib.kvf8_probe_gather.argtypes = [P, P, I64, I32, I32, I32, I32, I32, P, I32, P, I32, P, P]
+        lib.kvf8_probe_gather_split.restype = I32
+        lib.kvf8_probe_gather_split.argtypes = [P, P, I64, I32, I32, I32, I32, I32, P, I32, P, I32, I32, P, P]
         lib.kvf8_probe_rmw.restype = I32
         lib.kvf8_probe_rmw.argtypes = [P, I64, I32, I32, I32, I32, P, I64, P]
         lib.kvf8_probe_store_copy.restype = I32
@@ -103,3 +105,12 @@ def store_copy(k, v, k_stride: int, v_stride: int, slots, num_tokens: int, k_poo
     _check(_load().kvf8_probe_store_copy(_ptr(k), _ptr(v), k_stride, v_stride, _ptr(slots), num_tokens,
                                          _ptr(k_pool), _ptr(v_pool), num_blocks, kv_heads, block_size, head_dim,
                                          _stream(stream)))
+
+
+def gather_split(k_pool, v_pool, num_blocks: int, kv_heads: int, block_size: int, head_dim: int,
+                 k_elem_bytes: int, v_elem_bytes: int, block_tables, max_blocks: int, seq_lens, num_seqs: int,
+                 chunk_blocks: int, out_words, stream=None) -> None:
+    _check(_load().kvf8_probe_gather_split(_ptr(k_pool), _ptr(v_pool), num_blocks, kv_heads, block_size, head_dim,
+                                           k_elem_bytes, v_elem_bytes, _ptr(block_tables), max_blocks,
+                                           _ptr(seq_lens), num_seqs, chunk_blocks, _ptr(out_words),
+                                           _stream(stream)))

@@ -47,6 +47,19 @@ int kvf8_probe_gather(const void *k_pool, const void *v_pool, int64_t num_blocks
                       uint32_t *out_words, void *stream);
 
 /*
+ * The same read split the way a split-K decode reads: unit (c, b, h) reads
+ * table entries [c * chunk_blocks, (c + 1) * chunk_blocks) of sequence b's
+ * blocks (as limited above) for kv-head h and writes their XOR to
+ * out_words[(c * num_seqs + b) * num_kv_heads + h], for c < ceil(max_blocks /
+ * chunk_blocks) (units past a sequence's blocks write 0).  chunk_blocks > 0.
+ * kvf8_probe_gather is this call with one chunk per row.
+ */
+int kvf8_probe_gather_split(const void *k_pool, const void *v_pool, int64_t num_blocks, int32_t num_kv_heads,
+                            int32_t block_size, int32_t head_dim, int32_t k_elem_bytes, int32_t v_elem_bytes,
+                            const int32_t *block_tables, int32_t max_blocks, const int32_t *seq_lens, int32_t num_seqs,
+                            int32_t chunk_blocks, uint32_t *out_words, void *stream);
+
+/*
  * The memory traffic of kv_shift_rope's run path (NEOX pairing) with no
  * arithmetic: for every slot of `slots` (device, n_slots int64 entries;
  * entries < 0 or >= num_blocks * block_size are skipped, as by the K-shift)

@@ -59,6 +59,8 @@ struct GatherArgs {
     int32_t block_size;
     int32_t k_words_log2;    // log2 of the 16-byte words of one (block, head) tile
     int32_t v_words_log2;
+    int32_t chunk_blocks;    // table entries per unit (a unit reads one chunk of one pair's row)
+    int32_t chunks;          // chunks per row: ceil(max_blocks / chunk_blocks)
 };
 
 __global__ __launch_bounds__(kThreads) void read_probe(const u32x4 *buf, int64_t n16, uint32_t *out) {
@@ -106,11 +108,16 @@ __device__ __forceinline__ u32x4 gather_words(const u32x4 *pool, const int32_t *
 __global__ __launch_bounds__(kThreads) void gather_probe(GatherArgs a) {
     __shared__ int32_t ids[kGatherIds];
     const int unit = blockIdx.x;
-    const int seq = unit / a.kv_heads, head = unit - seq * a.kv_heads;
+    const int npairs = a.num_seqs * a.kv_heads;
+    const int pair = unit % npairs, chunk = unit / npairs;   // chunk-major: neighbouring units, other pairs
+    const int seq = pair / a.kv_heads, head = pair - seq * a.kv_heads;
     const int len = a.seq_lens[seq];
     int64_t nblk = len > 0 ? (len + a.block_size - 1) / a.block_size : 0;
     if (nblk > a.max_blocks) nblk = a.max_blocks;            // as the decode: never past the table row
-    const int32_t *table = a.block_tables + (int64_t)seq * a.max_blocks;
+    const int64_t first = (int64_t)chunk * a.chunk_blocks;
+    nblk = nblk > first ? nblk - first : 0;
+    if (nblk > a.chunk_blocks) nblk = a.chunk_blocks;
+    const int32_t *table = a.block_tables + (int64_t)seq * a.max_blocks + first;
     u32x4 acc = {0u, 0u, 0u, 0u};
     for (int64_t b0 = 0; b0 < nblk; b0 += kGatherIds) {
         const int nb = (int)(nblk - b0 < kGatherIds ? nblk - b0 : kGatherIds);
@@ -343,10 +350,11 @@ int kvf8_probe_read(const void *buf, size_t bytes, uint32_t *out_words, int32_t 
     return launched("kvf8_probe_read launch");
 }
 
-int kvf8_probe_gather(const void *k_pool, const void *v_pool, int64_t num_blocks, int32_t num_kv_heads,
-                      int32_t block_size, int32_t head_dim, int32_t k_elem_bytes, int32_t v_elem_bytes,
-                      const int32_t *block_tables, int32_t max_blocks, const int32_t *seq_lens, int32_t num_seqs,
-                      uint32_t *out_words, void *stream) {
+int kvf8_probe_gather_split(const void *k_pool, const void *v_pool, int64_t num_blocks, int32_t num_kv_heads,
+                            int32_t block_size, int32_t head_dim, int32_t k_elem_bytes, int32_t v_elem_bytes,
+                            const int32_t *block_tables, int32_t max_blocks, const int32_t *seq_lens, int32_t num_seqs,
+                            int32_t chunk_blocks, uint32_t *out_words, void *stream) {
+    if (chunk_blocks <= 0) return fail("chunk_blocks must be positive");
     if (num_seqs < 0 || max_blocks < 0) return fail("num_seqs and max_blocks must be >= 0");
     if (num_blocks <= 0 || num_kv_heads <= 0) return fail("num_blocks and num_kv_heads must be positive");
     if ((block_size != 16 && block_size != 32) || (head_dim != 64 && head_dim != 128 && head_dim != 256))
@@ -359,7 +367,8 @@ int kvf8_probe_gather(const void *k_pool, const void *v_pool, int64_t num_blocks
     }
     if (!k_pool || !v_pool || !block_tables || !seq_lens || !out_words)
         return fail("pools, block_tables, seq_lens and out_words must be non-NULL");
-    if ((int64_t)num_seqs * num_kv_heads > 0x7FFFFFFF) return fail("too many (sequence, kv-head) units");
+    const int64_t chunks = max_blocks > 0 ? ((int64_t)max_blocks + chunk_blocks - 1) / chunk_blocks : 1;
+    if ((int64_t)num_seqs * num_kv_heads * chunks > 0x7FFFFFFF) return fail("too many units");
     auto words_log2 = [&](int eb) {
         const int64_t words = (int64_t)block_size * head_dim * eb / 16;
         int l = 0;
@@ -379,9 +388,20 @@ int kvf8_probe_gather(const void *k_pool, const void *v_pool, int64_t num_blocks
     a.block_size = block_size;
     a.k_words_log2 = words_log2(k_elem_bytes);
     a.v_words_log2 = words_log2(v_elem_bytes);
-    hipLaunchKernelGGL(gather_probe, dim3((unsigned)(num_seqs * num_kv_heads)), dim3(kThreads), 0,
+    a.chunk_blocks = chunk_blocks;
+    a.chunks = (int32_t)chunks;
+    hipLaunchKernelGGL(gather_probe, dim3((unsigned)((int64_t)num_seqs * num_kv_heads * chunks)), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), a);
     return launched("kvf8_probe_gather launch");
+}
+
+int kvf8_probe_gather(const void *k_pool, const void *v_pool, int64_t num_blocks, int32_t num_kv_heads,
+                      int32_t block_size, int32_t head_dim, int32_t k_elem_bytes, int32_t v_elem_bytes,
+                      const int32_t *block_tables, int32_t max_blocks, const int32_t *seq_lens, int32_t num_seqs,
+                      uint32_t *out_words, void *stream) {
+    return kvf8_probe_gather_split(k_pool, v_pool, num_blocks, num_kv_heads, block_size, head_dim, k_elem_bytes,
+                                   v_elem_bytes, block_tables, max_blocks, seq_lens, num_seqs,
+                                   max_blocks > 0 ? max_blocks : 1, out_words, stream);
 }
 
 int kvf8_probe_rmw(void *k_pool, int64_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,

@@ -63,6 +63,39 @@ def test_gather_probe_xor(BS, Hkv, D, v_elem):
             assert int(got[b * Hkv + hh]) == int(want), (b, hh)
 
 
+@pytest.mark.parametrize("chunk", [1, 3, 8])
+def test_gather_split_probe_xor(chunk):
+    """The split read covers, per (chunk, sequence, kv-head), exactly that
+    chunk of the sequence's table entries: the XOR of their K and V tiles
+    (0 for chunks past the sequence's blocks)."""
+    rng = np.random.default_rng(7 + chunk)
+    BS, Hkv, D = 32, 2, 256
+    lens = np.array([0, 1, 33, 200, 8 * BS], np.int32)
+    NB, max_blocks = 48, 8
+    tables = rng.permutation(NB)[:lens.size * max_blocks].reshape(lens.size, max_blocks).astype(np.int32)
+    tile = BS * D
+    kp = rng.integers(0, 1 << 32, size=NB * Hkv * tile // 4, dtype=np.uint32)
+    vp = rng.integers(0, 1 << 32, size=NB * Hkv * tile // 4, dtype=np.uint32)
+    chunks = -(-max_blocks // chunk)
+    log(f"gather split probe chunk={chunk}")
+    out = torch.full((chunks * lens.size * Hkv,), -1, dtype=torch.int32, device=DEV)
+    probe.gather_split(torch.from_numpy(kp.view(np.int32)).to(DEV), torch.from_numpy(vp.view(np.int32)).to(DEV), NB,
+                       Hkv, BS, D, 1, 1, torch.from_numpy(tables).to(DEV), max_blocks, torch.from_numpy(lens).to(DEV),
+                       lens.size, chunk, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32)
+    kt, vt = kp.reshape(NB, Hkv, tile // 4), vp.reshape(NB, Hkv, tile // 4)
+    for c in range(chunks):
+        for b, L in enumerate(lens):
+            nblk = min(-(-int(L) // BS), max_blocks)
+            blocks = tables[b, c * chunk:min(nblk, (c + 1) * chunk)] if nblk > c * chunk else tables[b, :0]
+            for hh in range(Hkv):
+                want = np.uint32(0)
+                if blocks.size:
+                    want = np.bitwise_xor.reduce(np.concatenate([kt[blocks, hh].ravel(), vt[blocks, hh].ravel()]))
+                assert int(got[(c * lens.size + b) * Hkv + hh]) == int(want), (c, b, hh)
+
+
 @pytest.mark.parametrize("BS,Hkv,D,rot", [(16, 2, 64, 64), (32, 2, 256, 256), (16, 3, 128, 64), (16, 1, 64, 32)])
 def test_rmw_probe_touches_the_kshift_bytes(BS, Hkv, D, rot):
     """One pass flips bit 0 of exactly the rotated bytes (dims [0, rot)) of the

@@ -36,6 +36,12 @@ def test_gather_probe_host_checks():
             probe.gather(a["k"], a["v"], a["nb"], a["h"], a["bs"], a["d"], a["keb"], a["veb"], a["t"], a["mb"],
                          a["l"], a["n"], a["o"], 0)
         assert ei.value.status == E_INVALID, change
+    for change in bad + [dict(cb=0), dict(cb=-3)]:
+        a = {**good, "cb": 2, **change}
+        with pytest.raises(probe.ProbeError) as ei:
+            probe.gather_split(a["k"], a["v"], a["nb"], a["h"], a["bs"], a["d"], a["keb"], a["veb"], a["t"],
+                               a["mb"], a["l"], a["n"], a["cb"], a["o"], 0)
+        assert ei.value.status == E_INVALID, change
 
 
 def test_rmw_probe_host_checks():
