@@ -13,7 +13,8 @@
 // tiles through the block table (block ids staged in LDS, four 16-byte loads
 // in flight per lane, K tiles then V tiles) and writes their XOR.  Its rate
 // is the ceiling of the decode's access pattern (scattered tiles), as
-// opposed to a linear stream.
+// opposed to a linear stream.  kvf8_probe_gather_split gives each chunk of
+// a row's table entries a workgroup of its own, as a split-K decode does.
 //
 // kvf8_probe_rmw: the K-shift's memory traffic with no arithmetic.  The same
 // work items as the run path of the NEOX K-shift (a (slot, head) item and a
