@@ -1014,8 +1014,8 @@ def _library_tables(kv, handle, w, seed):
 def main():
     args = _parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the path shards by kv-head or sequence with no exchange, see the design notes)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              f"(the path shards by kv-head or sequence with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
