@@ -6,12 +6,15 @@
 // [P2, ggml_fp32_to_f8_e4m3].  Negative slots and slots past the pool are
 // skipped.
 //
-// One workgroup handles sixteen consecutive input tokens.  When they go to
-// sixteen consecutive slots starting at a multiple of 16 (every fill and
-// every prefill chunk: a whole block, or half of a 32-token block), the
-// workgroup writes each head's part of the K and V tiles as one contiguous
-// run (K: 16 tokens x D codes of a column-quarter layout; V: 4 groups of 4
-// tokens), each thread with several 16-byte loads in flight.  Otherwise each
+// One workgroup handles sixteen consecutive input tokens (in a call of few
+// tokens up to kv_heads workgroups share them, each taking a range of the
+// kv-heads, so that a decode step's append still spreads over the chip).
+// When they go to sixteen consecutive slots starting at a multiple of 16
+// (every fill and every prefill chunk: a whole block, or half of a 32-token
+// block), the workgroup writes each head's part of the K and V tiles as one
+// contiguous run (K: 16 tokens x D codes of a column-quarter layout; V: 4
+// groups of 4 tokens), each thread with several 16-byte loads in flight.
+// Otherwise each
 // of its four waves takes four of the tokens on the path below, where each
 // lane reads a 16-byte-aligned run of bf16 values (coalesced across the
 // wave) and writes whole 16-byte runs of codes:
@@ -36,6 +39,7 @@ namespace kvf8 {
 namespace {
 
 constexpr int kStoreThreads = 256;
+constexpr int64_t kMinStoreWgs = 1024;   // 4 workgroups per CU
 
 // Bit 15 of each half of w that holds a bf16 NaN (exponent all ones and a
 // nonzero fraction: magnitude bits above 0x7F80).
@@ -76,7 +80,7 @@ __device__ __forceinline__ u32x4 encode16(u32x4 lo, u32x4 hi, float inv) {
 // absent), each to its own slot.  KB / VB: element bytes of the K / V pool,
 // 1 (E4M3 codes) or 2 (the bf16 values as given, at the same positions).
 template <int KB, int VB>
-__device__ __forceinline__ void store_quad(const StoreArgs &a, int64_t tok0, int tid, int nthr) {
+__device__ __forceinline__ void store_quad(const StoreArgs &a, int64_t tok0, int tid, int nthr, int h0, int nh) {
     const int D = a.head_dim;
     const int H = a.kv_heads;
     const int BS = a.block_size;
@@ -88,8 +92,8 @@ __device__ __forceinline__ void store_quad(const StoreArgs &a, int64_t tok0, int
     uint8_t *__restrict__ vout = a.v_pool;
     const int runs = D >> 4;            // 16-dim runs per head
     const int quads = D >> 2;           // 4-dim runs per head
-    const int k_items = 4 * H * runs;   // 4 tokens x H heads x runs
-    const int v_items = H * quads;      // H heads x quads, each over the four tokens
+    const int k_items = 4 * nh * runs;  // 4 tokens x nh heads (h0 ..) x runs
+    const int v_items = nh * quads;     // nh heads x quads, each over the four tokens
 
     int64_t slot[4];
 #pragma unroll
@@ -104,10 +108,11 @@ __device__ __forceinline__ void store_quad(const StoreArgs &a, int64_t tok0, int
 
     // ---------------- K: 16 dims of one token -> one 16-byte run of codes
     for (int it = tid; it < k_items; it += nthr) {
-        const int k = it / (H * runs);
-        const int rem = it - k * (H * runs);
-        const int h = rem / runs;
-        const int r = rem - h * runs;
+        const int k = it / (nh * runs);
+        const int rem = it - k * (nh * runs);
+        const int hh = rem / runs;
+        const int r = rem - hh * runs;
+        const int h = h0 + hh;
         if (tok0 + k >= a.num_tokens) continue;
         const u32x4 *src = reinterpret_cast<const u32x4 *>(kin + (tok0 + k) * a.k_stride + (int64_t)h * D + r * 16);
         const u32x4 lo = src[0], hi = src[1];
@@ -130,8 +135,9 @@ __device__ __forceinline__ void store_quad(const StoreArgs &a, int64_t tok0, int
     const bool group = slot[0] >= 0 && (slot[0] & 3) == 0 && slot[1] == slot[0] + 1 &&
                        slot[2] == slot[0] + 2 && slot[3] == slot[0] + 3;
     for (int it = tid; it < v_items; it += nthr) {
-        const int h = it / quads;
-        const int d4 = it - h * quads;
+        const int hh = it / quads;
+        const int d4 = it - hh * quads;
+        const int h = h0 + hh;
         uint32_t b[4][4];   // [token][dim] bf16 bits
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -220,7 +226,7 @@ __device__ __forceinline__ void store_quad(const StoreArgs &a, int64_t tok0, int
 // Consecutive threads take consecutive pieces, so a wave's stores are
 // contiguous runs; each thread has all its loads in flight before it
 // encodes.
-__device__ __forceinline__ void store_run16(const StoreArgs &a, int64_t tok0, int64_t s0) {
+__device__ __forceinline__ void store_run16(const StoreArgs &a, int64_t tok0, int64_t s0, int h0, int nh) {
     const int D = a.head_dim;
     const int H = a.kv_heads;
     const int BS = a.block_size;
@@ -231,15 +237,16 @@ __device__ __forceinline__ void store_run16(const StoreArgs &a, int64_t tok0, in
     const int np = D >> 6;                // 16-code pieces per column quarter of a token
     const int kper = 16 * (D >> 4);       // K pieces per head: 16 tokens x D/16 runs
     const int vper = 4 * (D >> 3);        // V pieces per head: 4 groups x D/8 runs
-    const int k_items = H * kper, v_items = H * vper;
+    const int k_items = nh * kper, v_items = nh * vper;
     for (int base = 0; base < k_items; base += 4 * kStoreThreads) {
         u32x4 lo[4], hi[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int it = base + u * kStoreThreads + threadIdx.x;
             if (it < k_items) {
-                const int h = it / kper;
-                const int r = it - h * kper;                    // (q, t, j) in this order
+                const int hh = it / kper;
+                const int r = it - hh * kper;                   // (q, t, j) in this order
+                const int h = h0 + hh;
                 const int j = r % np, t = (r / np) & 15, q = r / (16 * np);
                 const u32x4 *src =
                     reinterpret_cast<const u32x4 *>(a.k + (tok0 + t) * a.k_stride + (int64_t)h * D + q * Q4 + j * 16);
@@ -251,8 +258,9 @@ __device__ __forceinline__ void store_run16(const StoreArgs &a, int64_t tok0, in
         for (int u = 0; u < 4; ++u) {
             const int it = base + u * kStoreThreads + threadIdx.x;
             if (it < k_items) {
-                const int h = it / kper;
-                const int r = it - h * kper;
+                const int hh = it / kper;
+                const int r = it - hh * kper;
+                const int h = h0 + hh;
                 const int j = r % np, t = (r / np) & 15, q = r / (16 * np);
                 const int64_t off = (blk * H + h) * tile + (int64_t)(q * BS + t0 + t) * Q4 + j * 16;
                 *reinterpret_cast<u32x4 *>(a.k_pool + off) = encode16(lo[u], hi[u], a.k_inv);
@@ -265,8 +273,9 @@ __device__ __forceinline__ void store_run16(const StoreArgs &a, int64_t tok0, in
         for (int u = 0; u < 2; ++u) {
             const int it = base + u * kStoreThreads + threadIdx.x;
             if (it < v_items) {
-                const int h = it / vper;
-                const int r = it - h * vper;                    // (g, o)
+                const int hh = it / vper;
+                const int r = it - hh * vper;                   // (g, o)
+                const int h = h0 + hh;
                 const int g = r / (D >> 3), o = r - g * (D >> 3);
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
@@ -278,8 +287,9 @@ __device__ __forceinline__ void store_run16(const StoreArgs &a, int64_t tok0, in
         for (int u = 0; u < 2; ++u) {
             const int it = base + u * kStoreThreads + threadIdx.x;
             if (it < v_items) {
-                const int h = it / vper;
-                const int r = it - h * vper;
+                const int hh = it / vper;
+                const int r = it - hh * vper;
+                const int h = h0 + hh;
                 const int g = r / (D >> 3), o = r - g * (D >> 3);
                 // dim j of the eight: bf16 j/2 of word j/2 ... of each token
                 u32x4 out[2];
@@ -320,6 +330,9 @@ __device__ __forceinline__ void store_run16(const StoreArgs &a, int64_t tok0, in
 template <int KB, int VB>
 __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a) {
     const int64_t tok0 = (int64_t)blockIdx.x * 16;
+    // kv-heads [h0, h0 + nh) of the 16 tokens: gridDim.y workgroups share a group's heads
+    const int h0 = (int)(((int64_t)blockIdx.y * a.kv_heads) / gridDim.y);
+    const int nh = (int)(((int64_t)(blockIdx.y + 1) * a.kv_heads) / gridDim.y) - h0;
     if constexpr (KB == 1 && VB == 1) {
         // the run test: 16 tokens present, slots s0 .. s0+15 with s0 % 16 == 0, inside the pool
         __shared__ int64_t s_first;
@@ -338,13 +351,13 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a) {
         }
         __syncthreads();
         if (s_run) {
-            store_run16(a, tok0, s_first);
+            store_run16(a, tok0, s_first, h0, nh);
             return;
         }
     }
     // otherwise wave w stores tokens tok0 + 4w .. + 3, the four waves side by side
     const int64_t quad = tok0 + 4 * (threadIdx.x >> 6);
-    if (quad < a.num_tokens) store_quad<KB, VB>(a, quad, threadIdx.x & 63, 64);
+    if (quad < a.num_tokens) store_quad<KB, VB>(a, quad, threadIdx.x & 63, 64, h0, nh);
 }
 
 }  // namespace
@@ -352,14 +365,21 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a) {
 hipError_t launch_store(const StoreArgs &a, hipStream_t stream) {
     const int64_t wgs = (a.num_tokens + 15) / 16;
     if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+    // Few tokens (a decode step's one token per sequence) would leave most of
+    // the chip idle: the kv-heads of a 16-token group are then split over up
+    // to kv_heads workgroups, so that at least ~kMinStoreWgs run.
+    int64_t split = (kMinStoreWgs + wgs - 1) / wgs;
+    if (split > a.kv_heads) split = a.kv_heads;
+    if (split < 1) split = 1;
+    const dim3 grid((unsigned)wgs, (unsigned)split);
     if (a.k_eb == 1 && a.v_eb == 1)
-        hipLaunchKernelGGL((store_kernel<1, 1>), dim3((unsigned)wgs), dim3(kStoreThreads), 0, stream, a);
+        hipLaunchKernelGGL((store_kernel<1, 1>), grid, dim3(kStoreThreads), 0, stream, a);
     else if (a.k_eb == 1)
-        hipLaunchKernelGGL((store_kernel<1, 2>), dim3((unsigned)wgs), dim3(kStoreThreads), 0, stream, a);
+        hipLaunchKernelGGL((store_kernel<1, 2>), grid, dim3(kStoreThreads), 0, stream, a);
     else if (a.v_eb == 1)
-        hipLaunchKernelGGL((store_kernel<2, 1>), dim3((unsigned)wgs), dim3(kStoreThreads), 0, stream, a);
+        hipLaunchKernelGGL((store_kernel<2, 1>), grid, dim3(kStoreThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((store_kernel<2, 2>), dim3((unsigned)wgs), dim3(kStoreThreads), 0, stream, a);
+        hipLaunchKernelGGL((store_kernel<2, 2>), grid, dim3(kStoreThreads), 0, stream, a);
     return hipGetLastError();
 }
 

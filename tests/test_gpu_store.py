@@ -5,8 +5,9 @@ a tiny scale that lifts fp32 subnormals into range, and saturation) through
 the 16-token run path (consecutive slots) and the token-by-token path
 (shuffled slots), runs and broken runs in one call, both the four-token-group
 and the single-token V write paths, negative slots,
-padded token strides, untouched bytes, library-owned pools, and the store
-shapes of each workload at reduced size.
+padded token strides, untouched bytes, library-owned pools, small calls whose
+kv-heads are split over several workgroups, and the store shapes of each
+workload at reduced size.
 """
 import ctypes
 
@@ -126,6 +127,32 @@ def test_store_sixteen_token_runs_and_broken_runs(BS, Hkv, D):
         ks, vs = kv.kv_cache_get_scales(c.handle, 0)
         gk, gv = _gpu_store(c, k, v, slots)
     base = np.full((NB, Hkv, BS * D), 0x5A, np.uint8)
+    ok, ov = _oracle_store(k, v, slots, NB, Hkv, D, BS, ks, vs, base, base)
+    assert np.array_equal(gk, ok), f"K bytes differ at {np.count_nonzero(gk != ok)} positions"
+    assert np.array_equal(gv, ov), f"V bytes differ at {np.count_nonzero(gv != ov)} positions"
+
+
+@pytest.mark.parametrize("Hkv", [1, 3, 8])
+@pytest.mark.parametrize("T", [1, 5, 16, 37, 64, 1000])
+def test_store_small_calls_split_heads(Hkv, T):
+    """Few tokens (a decode step: one token per sequence, scattered slots, or a
+    short chunk of consecutive slots) spread each 16-token group's kv-heads over
+    several workgroups; every head of every token must land exactly as the
+    oracle stores it, and nothing else may change."""
+    D, BS, NB = 64, 16, 160
+    rng = np.random.default_rng(1000 * Hkv + T)
+    if T % 2:
+        slots = rng.choice(NB * BS, size=T, replace=False).astype(np.int64)
+    else:
+        start = BS * int(rng.integers(0, NB - T // BS - 1))
+        slots = np.arange(start, start + T, dtype=np.int64)
+    k = rng.integers(0, 1 << 16, size=(T, Hkv, D), dtype=np.uint16)
+    v = rng.integers(0, 1 << 16, size=(T, Hkv, D), dtype=np.uint16)
+    log(f"store small call: Hkv={Hkv} T={T}")
+    with GpuCache(NB, BS, Hkv, D, 0.02, 0.05, fill=0x3C) as c:
+        ks, vs = kv.kv_cache_get_scales(c.handle, 0)
+        gk, gv = _gpu_store(c, k, v, slots)
+    base = np.full((NB, Hkv, BS * D), 0x3C, np.uint8)
     ok, ov = _oracle_store(k, v, slots, NB, Hkv, D, BS, ks, vs, base, base)
     assert np.array_equal(gk, ok), f"K bytes differ at {np.count_nonzero(gk != ok)} positions"
     assert np.array_equal(gv, ov), f"V bytes differ at {np.count_nonzero(gv != ov)} positions"
