@@ -78,11 +78,10 @@ struct StepRegs {
 // for them explicitly (below): the compiler's own wait placement drained
 // every outstanding load at the loop head.  That is only sound while the
 // register allocator neither copies, reuses nor spills a ring register
-// between its load and its wait.  ring_check.py proves that on the compiled
-// assembly of every all-E4M3 instance (a dataflow pass over the kernel's
-// branches and loop), and the build refuses to link a library that fails it;
-// the bf16 and mixed-type rings are heavier and use plain loads, whose waits
-// the compiler places itself.
+// between its load and its wait.  tests/test_decode_ring_asm.py proves that on
+// the compiled assembly of every all-E4M3 instance (a dataflow pass over the
+// kernel's branches and loop); the bf16 and mixed-type rings are heavier and
+// use plain loads, whose waits the compiler places itself.
 template <int KB, int VB>
 struct AsmRing { static constexpr bool ON = KB == 1 && VB == 1; };
 
