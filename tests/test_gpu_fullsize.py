@@ -153,12 +153,17 @@ def assert_both(got, want, what):
     assert err <= ATOL, f"{what}: fp32-output max |d| {err:.3g} > {ATOL}"
 
 
-@pytest.mark.parametrize("elems", [(kv.ELEM_E4M3, kv.ELEM_E4M3), (kv.ELEM_BF16, kv.ELEM_BF16)],
-                         ids=["e4m3", "bf16_twin"])
+ELEMS = [(kv.ELEM_E4M3, kv.ELEM_E4M3), (kv.ELEM_BF16, kv.ELEM_BF16), (kv.ELEM_E4M3, kv.ELEM_BF16),
+         (kv.ELEM_BF16, kv.ELEM_E4M3)]
+ELEM_IDS = ["e4m3", "bf16_twin", "e4m3k_bf16v", "bf16k_e4m3v"]
+
+
+@pytest.mark.parametrize("elems", ELEMS, ids=ELEM_IDS)
 def test_llama8b_full_size(elems):
     """64 x 4096 tokens, 32 q / 8 kv heads, D 128, block 16: one store launch
     over all 262,144 tokens, one decode launch; all bytes, all 2,048 heads.
-    Also for the bf16 twin the benchmark compares the E4M3 cache against."""
+    Also for the bf16 twin and the two mixed caches the benchmark times beside
+    the E4M3 cache."""
     w = Workload("llama8b", device=DEV)
     cache = FullCache(w, elems)
     try:
@@ -315,15 +320,17 @@ def test_longctx_full_size_with_shift():
         cache.close()
 
 
-def test_prefill_full_size():
+@pytest.mark.parametrize("elems", ELEMS, ids=ELEM_IDS)
+def test_prefill_full_size(elems):
     """4 sequences x (16384 cached + 2048-token chunk), 32 q / 8 kv heads: the
     chunk's store launch then one prefill launch; all bytes, and 8,192 (query,
     head) rows: the first and last 32 tokens of every chunk with all heads,
-    plus seeded rows in between."""
+    plus seeded rows in between.  For the E4M3 cache and for the bf16 twin and
+    mixed caches the benchmark times beside it."""
     w = Workload("prefill", device=DEV)
-    cache = FullCache(w)
+    cache = FullCache(w, elems)
     try:
-        log("prefill full: fill 4 x 16384 tokens, store 4 x 2048, prefill")
+        log(f"prefill full ({elems}): fill 4 x 16384 tokens, store 4 x 2048, prefill")
         cache.fill(w.lengths)
         n = w.spec.new_tokens
         row = w.Hkv * w.D
@@ -345,7 +352,7 @@ def test_prefill_full_size():
             got[dt] = out.float().cpu().numpy()
             assert np.isfinite(got[dt]).all()
             del out
-        orc = OraclePools(w, cache.ks, cache.vs)
+        orc = OraclePools(w, cache.ks, cache.vs, cache.keb, cache.veb)
         orc.store([(b, 0, int(w.total_lengths[b])) for b in range(w.B)])
         orc.check_bytes(cache, "prefill")
         rng = np.random.default_rng(14)
